@@ -1,0 +1,239 @@
+/*
+ * pkv.h - exact softmax attention over a paged KV cache, AMD MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Plain pointers and sizes only; no framework types.
+ *
+ * Pages this interface follows (cited by title and section):
+ *  [P1] "Long-context inference engineering truths 2026: PagedAttention, Ring
+ *       Attention and KV-cache offload from 128K to 1M context"
+ *       (blog.lonae.com): 2.1 block_size 16 and the waste bound; 2.2 the
+ *       block table, append_token and allocate_block; 3.1 online softmax.
+ *  [P2] "Unlocking long context: engineering practice and optimisation of
+ *       million-token LLM inference" (www.ybb.press/ai-applications/14576):
+ *       3.1 block pool + logical block table; 3.2 FP8 (E4M3) KV and
+ *       block-wise scaling; 4.1 attention definition and causal flash
+ *       attention call; 5.1 prefill is compute-bound, decode is
+ *       bandwidth-bound; 5.2 chunked prefill.
+ *  [P3] article at www.mhpn.cn/news/2466452: 1.1 softmax(QK^T/sqrt(d))V and
+ *       the O(n) per-step decode scan; 1.2 tiling + online softmax keeps the
+ *       flops and avoids the n x n matrix; 3.2 GQA.
+ *  [P4] "Sequence-parallel engineering for long-context LLM inference: Ring
+ *       Attention and distributed KV cache" (www.ybb.press/ai-applications/
+ *       14023): "numerically stable incremental softmax" (merge of per-shard
+ *       results by a max / log-sum-exp correction).
+ *
+ * Conventions
+ *  - Ownership: the caller owns every buffer.  Device entry points never
+ *    allocate device memory; split-KV decode takes a caller workspace sized by
+ *    pkv_decode_workspace_bytes.  Only allocator objects are created by the
+ *    library (host memory).
+ *  - Asynchrony: device entry points enqueue work on `stream` (a hipStream_t
+ *    passed as void*, NULL = the null stream) and return without waiting.
+ *    pkv_validate_tables is the one exception (it copies to the host).
+ *  - Errors: every function returns an int32 status, PKV_OK (0) or a negative
+ *    code.  Arguments are checked on the host first; when a check fails
+ *    nothing is launched.  pkv_status_str() names a code.
+ *  - Table contents are the caller's contract: entries that a sequence length
+ *    covers must be distinct valid physical ids.  Kernels never dereference an
+ *    id outside [0, num_blocks) (the tokens it would hold are skipped and the
+ *    result for that row is then unspecified); pkv_validate_tables reports such
+ *    entries and aliasing.
+ *  - Reentrancy: functions are reentrant; an allocator object is not
+ *    thread-safe.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad shape        */
+  PKV_ERR_UNSUPPORTED = -2,  /* valid but not implemented combination       */
+  PKV_ERR_NO_BLOCKS = -3,    /* allocator has too few free blocks            */
+  PKV_ERR_WORKSPACE = -4,    /* workspace missing or too small               */
+  PKV_ERR_DEVICE = -5,       /* a HIP runtime call failed                    */
+  PKV_ERR_BAD_TABLE = -6     /* pkv_validate_tables found a bad entry        */
+};
+
+/* ---- element types ----------------------------------------------------- */
+enum {
+  PKV_F32 = 0,       /* IEEE binary32                                          */
+  PKV_BF16 = 1,      /* bfloat16 (upper half of binary32), round-to-nearest-even */
+  PKV_FP8_E4M3 = 2   /* OCP E4M3FN: bias 7, max 448, 0x7F/0xFF NaN, no inf      */
+};
+
+#define PKV_BLOCK_SIZE 16   /* tokens per physical block [P1 2.1, P2 3.1] */
+#define PKV_SCALE_GROUP 64  /* tokens per FP8 scale [P2 3.2]              */
+
+/* ---- paged KV cache of one attention layer [P1 2.2, P2 3.1] -------------
+ * Physical block b, kv head h:
+ *   K page at k_cache + b*block_stride + h*16*head_dim elements, laid out
+ *     [16 tokens][head_dim]   (token-major: one token's key is contiguous);
+ *   V page at v_cache + b*block_stride + h*head_dim*16 elements, laid out
+ *     [head_dim][16 tokens]   (dimension-major: one dimension's 16 values are
+ *     contiguous).
+ * block_stride >= num_kv_heads*16*head_dim, counted in elements of kv_dtype,
+ * lets K and V share one interleaved allocation.  Pools must be 16-byte
+ * aligned and block_stride*elem_size a multiple of 16.
+ * E4M3 caches carry fp32 scales k_scale/v_scale [num_blocks][num_kv_heads]:
+ * element value = decode(code) * scale of its (block, head); otherwise NULL. */
+typedef struct pkv_cache_desc {
+  void* k_cache;
+  void* v_cache;
+  int64_t block_stride;
+  float* k_scale;
+  float* v_scale;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;   /* must be PKV_BLOCK_SIZE */
+  int32_t head_dim;     /* 64 or 128              */
+  int32_t kv_dtype;     /* PKV_F32 | PKV_BF16 | PKV_FP8_E4M3 */
+} pkv_cache_desc;
+
+const char* pkv_status_str(int32_t status);
+
+/* ---- host block allocator [P1 2.1-2.2] ------------------------------------
+ * A free list of physical block ids.  Blocks leave from the front of the free
+ * order; released blocks return to the back, in table order.  A sequence's
+ * table grows by one block exactly when a token opens a new logical block
+ * (token t needs logical block t/16), so a sequence of n tokens owns
+ * ceil(n/16) blocks and wastes 16*ceil(n/16) - n <= 15 slots. */
+typedef struct pkv_allocator pkv_allocator;
+
+/* free_order: host array of num_blocks distinct ids in [0, num_blocks)
+ * (a permutation), or NULL for 0..num_blocks-1.  *out receives the object. */
+int32_t pkv_allocator_create(int32_t num_blocks, const int32_t* free_order,
+                             pkv_allocator** out);
+/* Grow sequence `seq` (>= 0) to new_len tokens.  All-or-nothing: if fewer free
+ * blocks remain than needed, returns PKV_ERR_NO_BLOCKS and changes nothing.
+ * A sequence never shrinks (new_len below its length: PKV_ERR_INVALID_ARG).
+ * If table_row is not NULL the sequence's full table (up to max_blocks
+ * entries, host int32) is copied there and *num_blocks_out (nullable) gets
+ * its length; a table longer than max_blocks is PKV_ERR_INVALID_ARG (state is
+ * then unchanged). */
+int32_t pkv_allocator_reserve(pkv_allocator* a, int32_t seq, int64_t new_len,
+                              int32_t* table_row, int32_t max_blocks,
+                              int32_t* num_blocks_out);
+/* Return all of seq's blocks to the free list and forget the sequence. */
+int32_t pkv_allocator_release(pkv_allocator* a, int32_t seq);
+/* Unused slots in seq's last block (0 for an unknown sequence). */
+int32_t pkv_allocator_waste_slots(const pkv_allocator* a, int32_t seq, int64_t* out);
+int32_t pkv_allocator_free_count(const pkv_allocator* a, int32_t* out);
+void pkv_allocator_destroy(pkv_allocator* a);
+
+/* ---- kv_append: write new tokens into pool slots [P1 2.2] ----------------
+ * For token i < num_tokens: block = block_tables[seq_idx[i]*max_blocks_per_seq
+ * + pos[i]/16], slot = pos[i]%16; K page row `slot` <- k_new[i][h][:] and V
+ * page column `slot` <- v_new[i][h][:] for every kv head h.
+ * k_new, v_new: device [num_tokens][num_kv_heads][head_dim], src_dtype.
+ * seq_idx, pos: device int32 [num_tokens]; block_tables: device int32
+ * [num_seqs][max_blocks_per_seq].
+ * Same-type caches copy bits (src_dtype must equal kv_dtype).  E4M3 caches
+ * take PKV_F32 or PKV_BF16 sources and store E4M3(f32(x) * f32(1/scale)) with
+ * the scale of the destination (block, head), rounding to nearest-even and
+ * saturating at +-448; the scales must already be set (pkv_fp8_group_scales).
+ * Tokens whose seq_idx is outside [0, num_seqs), whose pos is negative or
+ * beyond the table, or whose block id is outside [0, num_blocks) are skipped.
+ * Two tokens naming the same slot race (one of them wins). */
+int32_t pkv_kv_append(const pkv_cache_desc* cache, const void* k_new, const void* v_new,
+                      int32_t src_dtype, int32_t num_tokens, const int32_t* seq_idx,
+                      const int32_t* pos, const int32_t* block_tables, int32_t num_seqs,
+                      int32_t max_blocks_per_seq, void* stream);
+
+/* ---- FP8 block-wise scales [P2 3.2] ----------------------------------------
+ * For one sequence's tokens [pos0, pos0 + num_tokens) with pos0 % 64 == 0:
+ * every 64-token group (aligned to token 0; the last may be shorter) and kv
+ * head gets scale = f32(amax / 448), amax = largest |x| over the group's
+ * tokens and head_dim (1.0 when that quotient is 0 or subnormal), separately
+ * for K (from k_src) and V (from v_src).  The scale is stored into
+ * k_scale/v_scale[block][head] of every block the group touches, so scales move
+ * with blocks.  k_src, v_src: device [num_tokens][num_kv_heads][head_dim] of
+ * src_dtype (PKV_F32 | PKV_BF16); table_row: device int32 [max_blocks]
+ * covering the tokens. Requires an E4M3 cache. */
+int32_t pkv_fp8_group_scales(const pkv_cache_desc* cache, const void* k_src, const void* v_src,
+                             int32_t src_dtype, int32_t num_tokens, int32_t pos0,
+                             const int32_t* table_row, int32_t max_blocks, void* stream);
+
+/* ---- split-KV decode [P2 5.1, P3 1.1, P1 3.1, P4 incremental softmax] ----
+ * One query per sequence b (the newest token, already appended) attends to
+ * every key t < seq_lens[b] of that sequence:
+ *   O[b][h] = sum_t softmax_t(scale * q[b][h] . K_t) V_t,
+ * K_t, V_t read from kv head h / (num_q_heads / num_kv_heads) [P3 3.2] through
+ * the block table.  The sequence's blocks are cut into partitions of
+ * partition_blocks blocks (0 = chosen by the library); each partition yields a
+ * partial (unnormalised O, max, sum) in the workspace and a second kernel
+ * merges them exactly by log-sum-exp.
+ * q: device [B][num_q_heads][head_dim], q_dtype (PKV_F32 | PKV_BF16);
+ * out: device [B][num_q_heads][head_dim] in q_dtype; out_lse: device fp32
+ * [B][num_q_heads] (natural log of the softmax denominator incl. max) or NULL;
+ * seq_lens: device int32 [B]; seq_lens[b] == 0 gives O = 0 and lse = -inf.
+ * scale == 0 means 1/sqrt(head_dim).  Requires num_q_heads % num_kv_heads == 0.
+ * E4M3 caches need q_dtype PKV_BF16.  ws: device buffer of at least
+ * pkv_decode_workspace_bytes(...) bytes, 256-byte aligned. */
+int32_t pkv_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t max_blocks_per_seq, int32_t partition_blocks,
+                                   size_t* bytes);
+int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q, int32_t q_dtype,
+                              int32_t B, int32_t num_q_heads, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
+                              int32_t partition_blocks, void* out, float* out_lse, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* ---- chunked causal prefill against paged KV [P2 4.1, P2 5.2, P3 1.2] ----
+ * Query rows q[r] (r < T) of one sequence sit at absolute positions q_pos0+r.
+ * Row r attends to keys t with kv_begin <= t < kv_end and, when causal, t <=
+ * q_pos0 + r, read through block_table (device int32 [max_blocks], covering
+ * kv_end).  q: device [T][num_q_heads][head_dim] bf16; head_dim 128.
+ * Exactly one output form:
+ *  - final:   out (device bf16 [T][num_q_heads][head_dim]) = normalised O,
+ *             out_lse (nullable, fp32 [T][num_q_heads]);
+ *  - partial: part_o (fp32 [T][num_q_heads][head_dim], unnormalised),
+ *             part_m (fp32 [T][num_q_heads], max score in natural units),
+ *             part_l (fp32 [T][num_q_heads], sum of exp(score - max)),
+ *             for combining KV shards with pkv_attn_lse_merge.
+ * A row with no visible key gets O = 0, m = -inf, l = 0 (lse = -inf). */
+int32_t pkv_paged_attn_prefill(const pkv_cache_desc* cache, const void* q, int32_t q_dtype,
+                               int32_t T, int32_t num_q_heads, int32_t q_pos0,
+                               const int32_t* block_table, int32_t max_blocks,
+                               int32_t kv_begin, int32_t kv_end, int32_t causal, float scale,
+                               void* out, float* out_lse, float* part_o, float* part_m,
+                               float* part_l, void* stream);
+
+/* ---- exact merge of KV-shard partials [P4 incremental softmax, P1 3.1] ---
+ * S partial states over disjoint key sets, part_o fp32 [S][rows][head_dim],
+ * part_m / part_l fp32 [S][rows] (as written by prefill's partial form):
+ *   M = max_s m_s,  a_s = exp(m_s - M),  L = sum_s a_s l_s,
+ *   O = sum_s a_s O_s / L.
+ * Parts with l == 0 or m == -inf contribute nothing; if all do, O = 0,
+ * M = -inf, L = 0.  out: device [rows][head_dim] of out_dtype (PKV_F32 |
+ * PKV_BF16); out_m, out_l (nullable, fp32 [rows]) receive (M, L) so merges
+ * compose; out_lse (nullable, fp32 [rows]) receives M + ln L. */
+int32_t pkv_attn_lse_merge(int32_t S, int64_t rows, int32_t head_dim, const float* part_o,
+                           const float* part_m, const float* part_l, void* out,
+                           int32_t out_dtype, float* out_m, float* out_l, float* out_lse,
+                           void* stream);
+
+/* ---- table check (debug) ---------------------------------------------------
+ * Copies block_tables / seq_lens (device) to the host after synchronising
+ * `stream`, and checks that every entry covered by seq_lens[b] (the first
+ * ceil(seq_lens[b]/16)) is in [0, num_blocks) and that no physical block is
+ * covered twice.  *first_bad (host) gets -1 when all is well, else the flat
+ * index b*max_blocks_per_seq + j of the first bad entry (status
+ * PKV_ERR_BAD_TABLE); a seq_len below 0 or beyond max_blocks_per_seq*16 is
+ * reported at index b*max_blocks_per_seq. */
+int32_t pkv_validate_tables(const int32_t* block_tables, const int32_t* seq_lens, int32_t B,
+                            int32_t max_blocks_per_seq, int32_t num_blocks, int64_t* first_bad,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

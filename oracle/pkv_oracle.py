@@ -88,16 +88,19 @@ class Allocator:
         self.lens: dict[int, int] = {}
 
     def reserve(self, seq: int, new_len: int) -> list[int]:
-        table = self.tables.setdefault(seq, [])
+        table = list(self.tables.get(seq, []))
         old_len = self.lens.get(seq, 0)
         if new_len < old_len:
             raise ValueError("a sequence never shrinks")
+        free = list(self.free)
         for t in range(old_len, new_len):
             block_id = t // self.block_size
             if block_id == len(table):           # token t opens a new logical block
-                if not self.free:
+                if not free:                     # all-or-nothing: nothing changes
                     raise OutOfBlocks(f"no free block for sequence {seq} token {t}")
-                table.append(self.free.pop(0))
+                table.append(free.pop(0))
+        self.free = free
+        self.tables[seq] = table
         self.lens[seq] = new_len
         return list(table)
 

@@ -302,6 +302,11 @@ def test_allocator_exhaustion_and_reuse():
     assert alloc.reserve(0, 33) == [2, 0, 1]
     with pytest.raises(O.OutOfBlocks):
         alloc.reserve(1, 1)
+    alloc2 = O.Allocator(3, [2, 0, 1])
+    alloc2.reserve(0, 16)
+    with pytest.raises(O.OutOfBlocks):          # needs 3 more, 2 free: nothing changes
+        alloc2.reserve(0, 64)
+    assert alloc2.free_count() == 2 and alloc2.waste_slots(0) == 0
     alloc.release(0)
     assert alloc.reserve(1, 16) == [2]
 
