@@ -277,6 +277,38 @@ def append(cache: Cache, k_new, v_new, seq_idx, pos, tables) -> Cache:
     return cache
 
 
+def append_sequence(cache: Cache, k_seq, v_seq, table_row, pos0: int = 0, heads=None,
+                    chunk: int = 4096) -> Cache:
+    """Write one sequence's contiguous tokens [pos0, pos0 + n) (k_seq, v_seq
+    [n, Hkv, d], element bits for f32 / bf16 caches, float32 values for E4M3)
+    block by block.  Same result as append() token by token; ``heads``
+    restricts the kv heads written."""
+    n = k_seq.shape[0]
+    heads = range(cache.hkv) if heads is None else list(heads)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        toks = pos0 + np.arange(c0, c1)
+        blocks = np.asarray(table_row)[toks // BLOCK]
+        for h in heads:
+            kx = np.asarray(k_seq[c0:c1, h, :])
+            vx = np.asarray(v_seq[c0:c1, h, :])
+            if cache.fmt == "e4m3":
+                inv_k = f32(np.float32(1.0) / cache.k_scale[blocks, h])
+                inv_v = f32(np.float32(1.0) / cache.v_scale[blocks, h])
+                kx = e4m3_encode(f32(f32(kx) * inv_k[:, None]))
+                vx = e4m3_encode(f32(f32(vx) * inv_v[:, None]))
+            i = 0
+            while i < c1 - c0:
+                t = int(toks[i])
+                off = t % BLOCK
+                cnt = min(BLOCK - off, c1 - c0 - i)
+                blk = int(blocks[i])
+                cache.k[blk, h, off:off + cnt, :] = kx[i:i + cnt]
+                cache.v[blk, h, :, off:off + cnt] = vx[i:i + cnt].T
+                i += cnt
+    return cache
+
+
 # --------------------------------------------------------------------------
 # a2: walk the block table; dequantise   [P1 2.2, P2 3.1, P2 3.2]
 # --------------------------------------------------------------------------
@@ -336,10 +368,11 @@ def _q_f64(q, fmt):
     return bf16_bits_to_f64(q) if fmt == "bf16" else np.asarray(q, dtype=np.float64)
 
 
-def decode(cache: Cache, q, q_fmt, tables, seq_lens, scale=None):
+def decode(cache: Cache, q, q_fmt, tables, seq_lens, scale=None, kv_heads=None):
     """One query per sequence (the newest token, already appended) attends to
     all seq_lens[b] keys.  q [B, Hq, d].  Returns dict of float64 arrays
-    o [B,Hq,d], o_un, m, l, lse [B,Hq]."""
+    o [B,Hq,d], o_un, m, l, lse [B,Hq]; ``kv_heads`` restricts the work to the
+    query heads of those kv heads (the other rows stay 0)."""
     q = _q_f64(q, q_fmt)
     B, Hq, d = q.shape
     G = Hq // cache.hkv
@@ -348,7 +381,7 @@ def decode(cache: Cache, q, q_fmt, tables, seq_lens, scale=None):
     out.update({k: np.zeros((B, Hq)) for k in ("m", "l", "lse")})
     for b in range(B):
         n = int(seq_lens[b])
-        for g in range(cache.hkv):
+        for g in (range(cache.hkv) if kv_heads is None else kv_heads):
             K, V = gather_kv(cache, tables[b], n, g)
             heads = slice(g * G, (g + 1) * G)
             vis = np.ones((G, n), dtype=bool)
@@ -395,7 +428,11 @@ def lse_merge(parts):
     """parts: list of (O~ [..., d], m [...], l [...]) float64 partial states
     over disjoint key sets.  Returns (O normalised, M, L) for the union; a
     part with l == 0 (no visible keys) contributes nothing."""
-    ms = np.stack([np.asarray(p[1], dtype=np.float64) for p in parts])
+    def live(m, l):          # a part that saw at least one key
+        return np.isfinite(m) & (l > 0)
+
+    ms = np.stack([np.where(live(np.asarray(p[1], np.float64), np.asarray(p[2], np.float64)),
+                            np.asarray(p[1], np.float64), -np.inf) for p in parts])
     M = ms.max(axis=0)
     empty = ~np.isfinite(M)
     Msafe = np.where(empty, 0.0, M)
@@ -403,9 +440,12 @@ def lse_merge(parts):
     Osum = np.zeros_like(np.asarray(parts[0][0], dtype=np.float64))
     for Ou, m, l in parts:
         m = np.asarray(m, dtype=np.float64)
-        alpha = np.where(np.isfinite(m), np.exp(np.where(np.isfinite(m), m, 0.0) - Msafe), 0.0)
-        L = L + alpha * np.asarray(l, dtype=np.float64)
-        Osum = Osum + alpha[..., None] * np.asarray(Ou, dtype=np.float64)
+        l = np.asarray(l, dtype=np.float64)
+        ok = live(m, l)
+        alpha = np.where(ok, np.exp(np.where(ok, m, 0.0) - Msafe), 0.0)
+        L = L + alpha * np.where(ok, l, 0.0)
+        # select, never multiply: an empty part's O~ may hold anything
+        Osum = Osum + np.where(ok[..., None], alpha[..., None] * np.asarray(Ou, np.float64), 0.0)
     with np.errstate(invalid="ignore", divide="ignore"):
         O = np.where((L > 0)[..., None], Osum / np.where(L > 0, L, 1.0)[..., None], 0.0)
     return O, np.where(empty, -np.inf, M), L

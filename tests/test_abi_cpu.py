@@ -1,0 +1,148 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared entry
+point, its host allocator follows the oracle allocator step for step, and
+argument checks fail before anything is launched (no GPU is used here)."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from oracle import pkv_oracle as O
+import synth
+from tests._util import header_symbols
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_cache_210_amd import lib as L
+    if not os.path.exists(L.LIB_PATH):
+        from paged_kv_cache_210_amd import build
+        build.build(verbose=False)
+    L.load()
+    return L
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = header_symbols()
+    assert len(syms) >= 14
+    so = ctypes.CDLL(lib.LIB_PATH)
+    missing = [s for s in syms if not hasattr(so, s)]
+    assert not missing, missing
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.status_str(code) and lib.status_str(code) != "unknown status"
+    assert lib.status_str(-99) == "unknown status"
+
+
+def test_allocator_matches_oracle_step_for_step(lib):
+    order = synth.free_order(64, 77).numpy()
+    a = lib.Allocator(64, order)
+    o = O.Allocator(64, order)
+    r = np.random.default_rng(1)
+    lens = {}
+    for step in range(400):
+        s = int(r.integers(0, 5))
+        if r.random() < 0.1:
+            a.release(s)
+            o.release(s)
+            lens.pop(s, None)
+        else:
+            n = lens.get(s, 0) + int(r.integers(0, 40))
+            try:
+                want = o.reserve(s, n)
+            except O.OutOfBlocks:
+                with pytest.raises(lib.PkvError) as e:
+                    a.reserve(s, n, max_blocks=64)
+                assert e.value.status == lib.PKV_ERR_NO_BLOCKS
+            else:
+                assert a.reserve(s, n, max_blocks=64) == want
+                lens[s] = n
+        assert a.free_count() == o.free_count()
+        for q in range(5):
+            assert a.waste_slots(q) == o.waste_slots(q)
+    a.close()
+
+
+def test_build_tables_match_oracle(lib):
+    cfg = synth.CONFIGS["C1"]
+    order = synth.free_order(cfg.pool_blocks, cfg.perm_seed)
+    t, w = lib.build_tables(cfg.seq_lens, cfg.pool_blocks, order)
+    to, wo = O.build_tables(cfg.seq_lens, cfg.pool_blocks, order.numpy())
+    np.testing.assert_array_equal(t.numpy(), to)
+    assert w == wo == [11, 12]
+
+
+def test_allocator_rejects_bad_input(lib):
+    with pytest.raises(lib.PkvError):
+        lib.Allocator(4, [0, 1, 1, 2])          # not a permutation
+    with pytest.raises(lib.PkvError):
+        lib.Allocator(0)
+    a = lib.Allocator(4)
+    a.reserve(0, 20)
+    with pytest.raises(lib.PkvError) as e:      # shrinking
+        a.reserve(0, 3)
+    assert e.value.status == lib.PKV_ERR_INVALID_ARG
+    with pytest.raises(lib.PkvError) as e:      # table longer than the caller's row
+        a.reserve(0, 40, max_blocks=2)
+    assert e.value.status == lib.PKV_ERR_INVALID_ARG and a.free_count() == 2
+
+
+def _desc(lib, **kw):
+    d = dict(k_cache=0x1000, v_cache=0x2000, block_stride=8 * 16 * 128, k_scale=None, v_scale=None,
+             num_blocks=10, num_kv_heads=8, block_size=16, head_dim=128, kv_dtype=lib.PKV_BF16)
+    d.update(kw)
+    return lib.CacheDesc(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_size=32), -2), (dict(head_dim=96), -2), (dict(kv_dtype=7), -1),
+    (dict(block_stride=100), -1), (dict(k_cache=None), -1), (dict(num_blocks=0), -1),
+    (dict(k_cache=0x1008), -1), (dict(kv_dtype=2), -1),      # E4M3 without scales
+])
+def test_cache_descriptor_checks_fail_before_launch(lib, kw, code):
+    L = lib.load()
+    d = _desc(lib, **kw)
+    st = L.pkv_kv_append(ctypes.byref(d), 0x3000, 0x4000, lib.PKV_BF16, 4, 0x5000, 0x6000, 0x7000,
+                         1, 4, None)
+    assert st == code
+
+
+def test_entry_point_argument_checks(lib):
+    L = lib.load()
+    d = _desc(lib)
+    size = ctypes.c_size_t()
+    # workspace query is pure host arithmetic
+    assert L.pkv_decode_workspace_bytes(ctypes.byref(d), lib.PKV_BF16, 4, 64, 8192, 256,
+                                        ctypes.byref(size)) == 0
+    assert size.value >= 4 * 64 * 32 * 128 * 4
+    assert L.pkv_decode_workspace_bytes(ctypes.byref(d), lib.PKV_BF16, 4, 60, 8192, 256,
+                                        ctypes.byref(size)) == lib.PKV_ERR_INVALID_ARG
+    # mismatched source dtype for a bf16 cache
+    assert L.pkv_kv_append(ctypes.byref(d), 0x3000, 0x4000, lib.PKV_F32, 4, 0x5000, 0x6000,
+                           0x7000, 1, 4, None) == lib.PKV_ERR_UNSUPPORTED
+    # decode: q heads not a multiple of kv heads; workspace too small
+    assert L.pkv_paged_attn_decode(ctypes.byref(d), 0x3000, lib.PKV_BF16, 2, 12, 0x4000, 4,
+                                   0x5000, 0.0, 0, 0x6000, None, 0x7000, 1 << 30,
+                                   None) == lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_paged_attn_decode(ctypes.byref(d), 0x3000, lib.PKV_BF16, 2, 16, 0x4000, 4,
+                                   0x5000, 0.0, 0, 0x6000, None, 0x7100, 16,
+                                   None) == lib.PKV_ERR_WORKSPACE
+    assert L.pkv_paged_attn_decode(ctypes.byref(d), 0x3000, lib.PKV_BF16, 2, 16, 0x4000, 4,
+                                   0x5000, float("nan"), 0, 0x6000, None, 0x7100, 1 << 30,
+                                   None) == lib.PKV_ERR_INVALID_ARG
+    # prefill: both output forms, then neither; kv range past the table
+    args = (ctypes.byref(d), 0x3000, lib.PKV_BF16, 8, 16, 0, 0x4000, 4, 0, 64, 1, 0.0)
+    assert L.pkv_paged_attn_prefill(*args, 0x5000, None, 0x6000, 0x7000, 0x8000,
+                                    None) == lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_paged_attn_prefill(*args, None, None, None, None, None,
+                                    None) == lib.PKV_ERR_INVALID_ARG
+    bad = (ctypes.byref(d), 0x3000, lib.PKV_BF16, 8, 16, 0, 0x4000, 4, 0, 65, 1, 0.0)
+    assert L.pkv_paged_attn_prefill(*bad, 0x5000, None, None, None, None,
+                                    None) == lib.PKV_ERR_INVALID_ARG
+    # merge: bad dims and dtype
+    assert L.pkv_attn_lse_merge(0, 4, 128, 0x1000, 0x2000, 0x3000, 0x4000, lib.PKV_BF16, None,
+                                None, None, None) == lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_attn_lse_merge(2, 4, 128, 0x1000, 0x2000, 0x3000, 0x4000, lib.PKV_FP8_E4M3, None,
+                                None, None, None) == lib.PKV_ERR_UNSUPPORTED

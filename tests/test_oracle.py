@@ -238,6 +238,10 @@ def test_merge_is_associative_and_all_empty_is_empty():
         np.testing.assert_allclose(x[0], y[0], rtol=1e-13, atol=1e-14)
         np.testing.assert_allclose(x[2] * np.exp(x[1] - y[1]), y[2], rtol=1e-13)
     E = part(0, empty=True)
+    stale = (np.full(shape + (8,), np.nan), np.full(shape, -np.inf), np.zeros(shape))
+    o3, m3, l3 = O.lse_merge([A, stale, B])
+    o4, m4, l4 = O.lse_merge([A, B])
+    np.testing.assert_array_equal(o3, o4)
     o, m, l = O.lse_merge([E, E])
     assert np.all(o == 0) and np.all(m == -np.inf) and np.all(l == 0)
     o2, m2, l2 = O.lse_merge([E, A, E])
@@ -434,3 +438,33 @@ def test_append_places_tokens_by_table():
     np.testing.assert_array_equal(cache.k[4, :, 8, :], k[2])
     np.testing.assert_array_equal(cache.v[4, :, :, 8], v[2])
     assert (cache.k == -7).sum() == cache.k.size - 3 * 16
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+def test_bulk_append_equals_token_append(fmt):
+    hkv, d, n = 2, 64, 150
+    g = torch.Generator().manual_seed(8)
+    k = torch.randn(n, hkv, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(n, hkv, d, generator=g).to(torch.bfloat16)
+    order = synth.free_order(14, 31).numpy()
+    tables, _ = O.build_tables([n], 14, order)
+    a = O.new_cache(14, hkv, d, fmt)
+    b = O.new_cache(14, hkv, d, fmt)
+    if fmt == "e4m3":
+        kk, vv = k.float().numpy(), v.float().numpy()
+        for c in (a, b):
+            O.fp8_group_scales(kk, 0, tables[0], c.k_scale)
+            O.fp8_group_scales(vv, 0, tables[0], c.v_scale)
+    else:
+        kk, vv = _bits(k), _bits(v)
+    O.append(a, kk, vv, np.zeros(n, np.int32), np.arange(n, dtype=np.int32), tables)
+    O.append_sequence(b, kk[:37], vv[:37], tables[0], 0, chunk=16)
+    O.append_sequence(b, kk[37:], vv[37:], tables[0], 37, chunk=50)
+    np.testing.assert_array_equal(a.k, b.k)
+    np.testing.assert_array_equal(a.v, b.v)
+    c = O.new_cache(14, hkv, d, fmt)
+    if fmt == "e4m3":
+        c.k_scale[:], c.v_scale[:] = a.k_scale, a.v_scale
+    O.append_sequence(c, kk, vv, tables[0], 0, heads=[1])
+    np.testing.assert_array_equal(c.k[:, 1], a.k[:, 1])
+    assert not c.k[:, 0].any()
