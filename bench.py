@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Throughput of the paged-attention hot path on one MI355X.
+
+A decode step is one pass of the whole decode path over one batch: append the
+newest token of every sequence into the paged pool (pkv_kv_append), then
+split-KV attention of that token against every cached key plus the exact
+log-sum-exp merge (pkv_paged_attn_decode).  Inputs are resident in HBM before
+the timed region starts.
+
+The headline line is the Llama-3-8B-like layer (32 sequences x 8192 tokens,
+32 q / 8 kv heads, d 128, bf16).  The 128K decode, the 1M-token E4M3 decode and
+the chunked causal prefill are reported under "secondary".  The fp64 CPU oracle
+is timed on a bounded sample of the headline workload as "cpu_baseline".
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode tok/s + HBM GB/s (% peak); prefill TFLOPS (% MFMA peak) @128K"
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _decode_setup(cfg, partition_blocks):
+    import torch
+    from paged_kv_cache_210_amd import lib
+    import synth
+
+    dev = "cuda"
+    inp = synth.decode_inputs(cfg, device=dev)
+    tables, _ = lib.build_tables(cfg.seq_lens, cfg.pool_blocks, inp["free_order"])
+    td = tables.to(dev)
+    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, cfg.kv_dtype, device=dev)
+    lens_l = list(cfg.seq_lens)
+    ends = torch.tensor(lens_l, device=dev).cumsum(0) - 1          # newest token of each seq
+    keep = torch.ones(cfg.num_tokens, dtype=torch.bool, device=dev)
+    keep[ends] = False
+    seq_idx, pos = inp["seq_idx"].to(dev), inp["pos"].to(dev)
+    if cfg.kv_dtype == "e4m3":
+        start = 0
+        for b, n in enumerate(lens_l):
+            lib.fp8_group_scales(cache, inp["k"][start:start + n], inp["v"][start:start + n], 0,
+                                 td[b])
+            start += n
+    lib.kv_append(cache, inp["k"][keep].contiguous(), inp["v"][keep].contiguous(), seq_idx[keep].contiguous(),
+                  pos[keep].contiguous(), td)
+    step_in = {
+        "k": inp["k"][ends].contiguous(), "v": inp["v"][ends].contiguous(),
+        "seq": torch.arange(cfg.batch, dtype=torch.int32, device=dev),
+        "pos": torch.tensor([n - 1 for n in lens_l], dtype=torch.int32, device=dev),
+    }
+    q = inp["q"]
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=dev)
+    ws = lib.decode_workspace(cache, q, td, partition_blocks)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    del inp, keep
+    torch.cuda.synchronize()
+    return dict(cache=cache, td=td, q=q, lens=lens, ws=ws, out=out, lse=lse, step_in=step_in,
+                tables=tables)
+
+
+def bench_decode(cfg, steps, warmup, partition_blocks=0):
+    """Returns (ms per step, ms per decode call, state)."""
+    import torch
+    from paged_kv_cache_210_amd import lib
+
+    st = _decode_setup(cfg, partition_blocks)
+    s = st["step_in"]
+
+    def step(ev0=None, ev1=None):
+        lib.kv_append(st["cache"], s["k"], s["v"], s["seq"], s["pos"], st["td"])
+        if ev0 is not None:
+            ev0.record()
+        lib.paged_attn_decode(st["cache"], st["q"], st["td"], st["lens"],
+                              partition_blocks=partition_blocks, out=st["out"],
+                              out_lse=st["lse"], ws=st["ws"])
+        if ev1 is not None:
+            ev1.record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(e0[i], e1[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    dec = sorted(e0[i].elapsed_time(e1[i]) for i in range(steps))
+    ms_dec = sum(dec) / len(dec)
+    return ms_step, ms_dec, st
+
+
+def decode_record(cfg, steps, warmup, partition_blocks):
+    from paged_kv_cache_210_amd import accounting as A
+
+    ms_step, ms_dec, st = bench_decode(cfg, steps, warmup, partition_blocks)
+    kbytes = A.decode_kernel_bytes(cfg.seq_lens, cfg.hq, cfg.hkv, cfg.head_dim, cfg.q_dtype,
+                                   cfg.kv_dtype)
+    step_bytes = A.decode_step_bytes(cfg.seq_lens, cfg.hq, cfg.hkv, cfg.head_dim, cfg.q_dtype,
+                                     cfg.kv_dtype)
+    gbs = kbytes / (ms_dec * 1e-3) / 1e9
+    rec = {
+        "workload": cfg.name,
+        "tok_per_s": cfg.batch / (ms_step * 1e-3),
+        "ms_per_step": ms_step,
+        "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / A.HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "pkv_paged_attn_decode (split-KV partial + LSE merge)",
+                     "ms_per_launch": ms_dec, "bytes_per_launch": kbytes},
+    }
+    return rec, st
+
+
+def _prefill_setup(cfg):
+    import torch
+    from paged_kv_cache_210_amd import lib
+    import synth
+
+    dev = "cuda"
+    inp = synth.prefill_inputs(cfg, device=dev)
+    tables, _ = lib.build_tables([cfg.prompt_len], cfg.pool_blocks, inp["free_order"])
+    td = tables.to(dev)
+    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16", device=dev)
+    C, S = cfg.chunk, cfg.shard_len
+    max_parts = -(-cfg.prompt_len // S)
+    part = (torch.empty(max_parts, C, cfg.hq, cfg.head_dim, dtype=torch.float32, device=dev),
+            torch.empty(max_parts, C, cfg.hq, dtype=torch.float32, device=dev),
+            torch.empty(max_parts, C, cfg.hq, dtype=torch.float32, device=dev))
+    out = torch.empty_like(inp["q"])
+    pos = torch.arange(cfg.prompt_len, dtype=torch.int32, device=dev)
+    seq = torch.zeros(C, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    return dict(inp=inp, td=td, cache=cache, part=part, out=out, pos=pos, seq=seq)
+
+
+def prefill_pass(cfg, st, ev=None):
+    """One chunked pass over the prompt: per chunk append its K/V, attend to
+    each visible KV shard (partial form), merge the shards by LSE."""
+    from paged_kv_cache_210_amd import lib
+
+    C, S = cfg.chunk, cfg.shard_len
+    inp, td, cache, (po, pm, pl) = st["inp"], st["td"], st["cache"], st["part"]
+    for c in range(cfg.num_chunks):
+        a, b = c * C, min((c + 1) * C, cfg.prompt_len)
+        lib.kv_append(cache, inp["k"][a:b], inp["v"][a:b], st["seq"][:b - a], st["pos"][a:b], td)
+        q = inp["q"][a:b]
+        nsh = -(-b // S)
+        if ev is not None:
+            ev.append(("start", c))
+        for j in range(nsh):
+            lib.paged_attn_prefill(cache, q, a, td[0], j * S, min((j + 1) * S, b), True,
+                                   partial=True, part=(po[j, :b - a], pm[j, :b - a], pl[j, :b - a]))
+        lib.attn_lse_merge(po[:nsh, :b - a], pm[:nsh, :b - a], pl[:nsh, :b - a],
+                           out=st["out"][a:b], with_state=False)
+        if ev is not None:
+            ev.append(("end", c))
+
+
+def prefill_record(cfg, reps):
+    import torch
+    from paged_kv_cache_210_amd import accounting as A
+
+    st = _prefill_setup(cfg)
+    prefill_pass(cfg, st)                      # warm-up pass
+    torch.cuda.synchronize()
+    marks = []
+    events = {}
+
+    class _Ev(list):
+        def append(self, item):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            events[item] = e
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    attn_ms = 0.0
+    start.record()
+    for _ in range(reps):
+        events.clear()
+        ev = _Ev()
+        prefill_pass(cfg, st, ev)
+        torch.cuda.synchronize()
+        attn_ms += sum(events[("start", c)].elapsed_time(events[("end", c)])
+                       for c in range(cfg.num_chunks))
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end) / reps
+    attn_ms /= reps
+    flops = A.causal_prompt_flops(cfg.prompt_len, cfg.hq, cfg.head_dim)
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    del st
+    torch.cuda.empty_cache()
+    return {
+        "workload": cfg.name,
+        "prompt_tok_per_s": cfg.prompt_len / (total_ms * 1e-3),
+        "ms_per_prompt": total_ms,
+        "attn_ms_per_prompt": attn_ms,
+        "tflops": tflops,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": A.BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / A.BF16_MFMA_PEAK_TFLOPS,
+                     "traffic": None,
+                     "kernel": "pkv_paged_attn_prefill (all shards) + pkv_attn_lse_merge",
+                     "flops_per_prompt": flops},
+    }
+
+
+def cpu_baseline_decode(cfg, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same decode
+    step: append the newest token of each sampled sequence, then attention over
+    all its keys.  Sequences are added until the budget is used."""
+    import numpy as np
+    import torch
+    from oracle import pkv_oracle as O
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas_threads = 1
+    inp = synth.decode_inputs(cfg, device="cuda")
+    order = inp["free_order"].numpy()
+    tables, _ = O.build_tables(cfg.seq_lens, cfg.pool_blocks, order)
+
+    def bits(t):
+        return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    cache = O.new_cache(cfg.pool_blocks, cfg.hkv, cfg.head_dim, cfg.kv_dtype)
+    q = bits(inp["q"])
+    done, spent = 0, 0.0
+    start = 0
+    for b, n in enumerate(cfg.seq_lens):
+        k = bits(inp["k"][start:start + n])
+        v = bits(inp["v"][start:start + n])
+        O.append_sequence(cache, k[:n - 1], v[:n - 1], tables[b], 0)        # untimed pre-fill
+        t0 = time.perf_counter()
+        O.append(cache, k[n - 1:n], v[n - 1:n], np.array([b], np.int32),
+                 np.array([n - 1], np.int32), tables)
+        O.decode(cache, q[b:b + 1], "bf16", tables[b:b + 1], [n])
+        spent += time.perf_counter() - t0
+        done += 1
+        start += n
+        if spent >= budget_s:
+            break
+    return {"value": done / spent, "unit": "tok/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences of {cfg.name} (append newest token + "
+                      f"decode over {cfg.seq_lens[0]} keys, all {cfg.hq} heads), "
+                      f"{spent:.1f} s of CPU time",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["C2", "C3", "C5", "C4", "C4_128K"],
+                    help="run one workload and print its record (for profiling)")
+    ap.add_argument("--prefill-reps", type=int, default=2)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(see the sharding notes); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    from paged_kv_cache_210_amd import lib
+
+    lib.load()
+    torch.cuda.init()
+    if args.only:
+        c = synth.CONFIGS[args.only]
+        _log(f"[bench] only {c.name}")
+        if args.only.startswith("C4"):
+            rec = prefill_record(c, args.prefill_reps)
+        else:
+            rec, _ = decode_record(c, args.steps, args.warmup,
+                                   0 if args.only == "C2" else 256)
+        print(json.dumps(rec), flush=True)
+        return 0
+    cfg = synth.CONFIGS["C2"]
+    _log(f"[bench] headline {cfg.name}: warmup {args.warmup}, steps {args.steps}")
+    head, st = decode_record(cfg, args.steps, args.warmup, 0)
+    del st
+    torch.cuda.empty_cache()
+    _log(f"[bench] {head['tok_per_s']:.0f} tok/s, decode {head['roofline']['achieved']:.0f} GB/s")
+
+    secondary = []
+    if not args.no_secondary:
+        for name, pb in (("C3", 256), ("C5", 256)):
+            c = synth.CONFIGS[name]
+            _log(f"[bench] secondary {c.name}")
+            rec, st = decode_record(c, args.steps, args.warmup, pb)
+            del st
+            torch.cuda.empty_cache()
+            rec["partition_blocks"] = pb
+            secondary.append(rec)
+            _log(f"[bench]   {rec['tok_per_s']:.0f} tok/s, {rec['roofline']['achieved']:.0f} GB/s")
+
+        for name in ("C4", "C4_128K"):
+            c = synth.CONFIGS[name]
+            _log(f"[bench] secondary {c.name}")
+            rec = prefill_record(c, args.prefill_reps)
+            secondary.append(rec)
+            _log(f"[bench]   {rec['tflops']:.0f} TFLOP/s, {rec['ms_per_prompt']:.2f} ms/prompt")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("[bench] cpu baseline (fp64 oracle)")
+        cpu = cpu_baseline_decode(cfg, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": head["tok_per_s"],
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v, shuffled physical blocks",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_lens[0],
+                   "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
+                   "block_size": 16, "kv_dtype": cfg.kv_dtype, "pool_blocks": cfg.pool_blocks,
+                   "step": "kv_append(1 token/seq) + split-KV decode + LSE merge"},
+        "decode_hbm_gbs": head["roofline"]["achieved"],
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

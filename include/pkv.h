@@ -176,10 +176,13 @@ int32_t pkv_fp8_group_scales(const pkv_cache_desc* cache, const void* k_src, con
  * seq_lens: device int32 [B]; seq_lens[b] == 0 gives O = 0 and lse = -inf.
  * scale == 0 means 1/sqrt(head_dim).  Requires num_q_heads % num_kv_heads == 0.
  * E4M3 caches need q_dtype PKV_BF16.  ws: device buffer of at least
- * pkv_decode_workspace_bytes(...) bytes, 256-byte aligned. */
-int32_t pkv_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
-                                   int32_t max_blocks_per_seq, int32_t partition_blocks,
-                                   size_t* bytes);
+ * pkv_decode_workspace_bytes(cache, q_dtype, B, num_q_heads,
+ * max_blocks_per_seq, partition_blocks) bytes, 256-byte aligned; it holds
+ * fp32 partials only, needs no initialisation, and may be reused by the
+ * next call once this one has finished on the stream. */
+int32_t pkv_decode_workspace_bytes(const pkv_cache_desc* cache, int32_t q_dtype, int32_t B,
+                                   int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                   int32_t partition_blocks, size_t* bytes);
 int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q, int32_t q_dtype,
                               int32_t B, int32_t num_q_heads, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,

@@ -1,0 +1,248 @@
+// C ABI of libpkv: host-side argument checks, then kernel launches.
+// Nothing is launched when a check fails; device entry points never allocate
+// and never synchronise (pkv_validate_tables excepted).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "pkv.h"
+#include "pkv_common.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+int32_t check_cache(const pkv_cache_desc* c) {
+  if (!c || !c->k_cache || !c->v_cache) return PKV_ERR_INVALID_ARG;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+  if (c->block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  const int es = elem_size(c->kv_dtype);
+  if (!es) return PKV_ERR_INVALID_ARG;
+  const int64_t min_stride = (int64_t)c->num_kv_heads * PKV_BLOCK_SIZE * c->head_dim;
+  if (c->block_stride < min_stride) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(c->k_cache) || !aligned16(c->v_cache) || ((c->block_stride * es) & 15))
+    return PKV_ERR_INVALID_ARG;
+  if (c->kv_dtype == PKV_FP8_E4M3 && (!c->k_scale || !c->v_scale)) return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+pkv::CacheView view(const pkv_cache_desc* c) {
+  return pkv::CacheView{c->k_cache, c->v_cache, c->block_stride, c->k_scale, c->v_scale,
+                        c->num_blocks, c->num_kv_heads, c->head_dim, c->kv_dtype};
+}
+
+int32_t from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_DEVICE; }
+
+hipStream_t stream_of(void* s) { return static_cast<hipStream_t>(s); }
+
+bool resolve_scale(float scale, int d, float* out) {
+  if (!std::isfinite(scale)) return false;
+  *out = scale == 0.0f ? 1.0f / std::sqrt((float)d) : scale;
+  return true;
+}
+
+}  // namespace
+
+extern "C" const char* pkv_status_str(int32_t status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported combination";
+    case PKV_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_DEVICE: return "HIP runtime error";
+    case PKV_ERR_BAD_TABLE: return "block table entry out of range or aliased";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int32_t pkv_kv_append(const pkv_cache_desc* cache, const void* k_new,
+                                 const void* v_new, int32_t src_dtype, int32_t num_tokens,
+                                 const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* block_tables, int32_t num_seqs,
+                                 int32_t max_blocks_per_seq, void* stream) {
+  int32_t st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0 || num_seqs <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+  if (cache->kv_dtype == PKV_FP8_E4M3) {
+    if (src_dtype != PKV_F32 && src_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  } else if (src_dtype != cache->kv_dtype) {
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !seq_idx || !pos || !block_tables) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_kv_append(view(cache), cache->k_cache, cache->v_cache, k_new, v_new,
+                                        src_dtype, num_tokens, seq_idx, pos, block_tables,
+                                        num_seqs, max_blocks_per_seq, stream_of(stream)));
+}
+
+extern "C" int32_t pkv_fp8_group_scales(const pkv_cache_desc* cache, const void* k_src,
+                                        const void* v_src, int32_t src_dtype, int32_t num_tokens,
+                                        int32_t pos0, const int32_t* table_row, int32_t max_blocks,
+                                        void* stream) {
+  int32_t st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (cache->kv_dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (src_dtype != PKV_F32 && src_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || pos0 < 0 || (pos0 % PKV_SCALE_GROUP) || max_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_src || !v_src || !table_row) return PKV_ERR_INVALID_ARG;
+  if ((int64_t)pos0 + num_tokens > (int64_t)max_blocks * PKV_BLOCK_SIZE) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_fp8_group_scales(view(cache), cache->k_scale, cache->v_scale, k_src,
+                                               v_src, src_dtype, num_tokens, pos0, table_row,
+                                               max_blocks, stream_of(stream)));
+}
+
+extern "C" int32_t pkv_decode_workspace_bytes(const pkv_cache_desc* cache, int32_t q_dtype,
+                                              int32_t B, int32_t num_q_heads,
+                                              int32_t max_blocks_per_seq,
+                                              int32_t partition_blocks, size_t* bytes) {
+  int32_t st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (!bytes || B < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % cache->num_kv_heads) return PKV_ERR_INVALID_ARG;
+  if (q_dtype != PKV_F32 && q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  *bytes = pkv::plan_decode(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                            max_blocks_per_seq, partition_blocks, q_dtype, cache->kv_dtype)
+               .ws_bytes;
+  return PKV_OK;
+}
+
+extern "C" int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q,
+                                         int32_t q_dtype, int32_t B, int32_t num_q_heads,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* seq_lens, float scale,
+                                         int32_t partition_blocks, void* out, float* out_lse,
+                                         void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (q_dtype != PKV_F32 && q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (B < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % cache->num_kv_heads) return PKV_ERR_INVALID_ARG;
+  if (cache->kv_dtype == PKV_FP8_E4M3 && q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  float sc;
+  if (!resolve_scale(scale, cache->head_dim, &sc)) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!q || !block_tables || !seq_lens || !out) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out)) return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  pkv::DecodePlan plan = pkv::plan_decode(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                          max_blocks_per_seq, partition_blocks, q_dtype,
+                                          cache->kv_dtype);
+  if (!ws || ws_bytes < plan.ws_bytes || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return PKV_ERR_WORKSPACE;
+  return from_hip(pkv::launch_decode(view(cache), q, q_dtype, B, num_q_heads, block_tables,
+                                     max_blocks_per_seq, seq_lens, sc, plan, out, out_lse, ws,
+                                     stream_of(stream)));
+}
+
+extern "C" int32_t pkv_paged_attn_prefill(const pkv_cache_desc* cache, const void* q,
+                                          int32_t q_dtype, int32_t T, int32_t num_q_heads,
+                                          int32_t q_pos0, const int32_t* block_table,
+                                          int32_t max_blocks, int32_t kv_begin, int32_t kv_end,
+                                          int32_t causal, float scale, void* out, float* out_lse,
+                                          float* part_o, float* part_m, float* part_l,
+                                          void* stream) {
+  int32_t st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (q_dtype != PKV_BF16 || cache->kv_dtype != PKV_BF16 || cache->head_dim != 128)
+    return PKV_ERR_UNSUPPORTED;
+  if (T < 0 || num_q_heads <= 0 || q_pos0 < 0 || max_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % cache->num_kv_heads) return PKV_ERR_INVALID_ARG;
+  if (kv_begin < 0 || kv_end < kv_begin || (int64_t)kv_end > (int64_t)max_blocks * PKV_BLOCK_SIZE)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)q_pos0 + T > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  const bool final_form = out != nullptr;
+  const bool part_form = part_o || part_m || part_l;
+  if (final_form == part_form) return PKV_ERR_INVALID_ARG;
+  if (part_form && (!part_o || !part_m || !part_l)) return PKV_ERR_INVALID_ARG;
+  float sc;
+  if (!resolve_scale(scale, cache->head_dim, &sc)) return PKV_ERR_INVALID_ARG;
+  if (T == 0) return PKV_OK;
+  if (!q || !block_table || !aligned16(q)) return PKV_ERR_INVALID_ARG;
+  if ((final_form && !aligned16(out)) || (part_form && !aligned16(part_o)))
+    return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_prefill(view(cache), q, T, num_q_heads, q_pos0, block_table,
+                                      max_blocks, kv_begin, kv_end, causal != 0, sc, out, out_lse,
+                                      part_o, part_m, part_l, stream_of(stream)));
+}
+
+extern "C" int32_t pkv_attn_lse_merge(int32_t S, int64_t rows, int32_t head_dim,
+                                      const float* part_o, const float* part_m,
+                                      const float* part_l, void* out, int32_t out_dtype,
+                                      float* out_m, float* out_l, float* out_lse, void* stream) {
+  if (S <= 0 || rows < 0 || head_dim <= 0 || head_dim > 256) return PKV_ERR_INVALID_ARG;
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (rows == 0) return PKV_OK;
+  if (rows > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (!part_o || !part_m || !part_l || !out) return PKV_ERR_INVALID_ARG;
+  pkv::MergeArgs a{};
+  a.S = S;
+  a.rows = rows;
+  a.D = head_dim;
+  a.o = part_o;
+  a.o_row = head_dim;
+  a.o_part = rows * head_dim;
+  a.m = part_m;
+  a.l = part_l;
+  a.ml_row = 1;
+  a.ml_part = rows;
+  a.m_log2 = false;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.out_m = out_m;
+  a.out_l = out_l;
+  a.out_lse = out_lse;
+  return from_hip(pkv::launch_merge(a, stream_of(stream)));
+}
+
+extern "C" int32_t pkv_validate_tables(const int32_t* block_tables, const int32_t* seq_lens,
+                                       int32_t B, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                       int64_t* first_bad, void* stream) {
+  if (!first_bad || B < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  *first_bad = -1;
+  if (B == 0) return PKV_OK;
+  if (!block_tables || !seq_lens) return PKV_ERR_INVALID_ARG;
+  std::vector<int32_t> tab((size_t)B * max_blocks_per_seq), lens(B);
+  hipStream_t s = stream_of(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return PKV_ERR_DEVICE;
+  if (hipMemcpy(tab.data(), block_tables, tab.size() * sizeof(int32_t), hipMemcpyDeviceToHost) !=
+          hipSuccess ||
+      hipMemcpy(lens.data(), seq_lens, lens.size() * sizeof(int32_t), hipMemcpyDeviceToHost) !=
+          hipSuccess)
+    return PKV_ERR_DEVICE;
+  std::vector<char> used(num_blocks, 0);
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t n = lens[b];
+    if (n < 0 || n > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE) {
+      *first_bad = (int64_t)b * max_blocks_per_seq;
+      return PKV_ERR_BAD_TABLE;
+    }
+    const int64_t nb = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t id = tab[(size_t)b * max_blocks_per_seq + j];
+      if (id < 0 || id >= num_blocks || used[id]) {
+        *first_bad = (int64_t)b * max_blocks_per_seq + j;
+        return PKV_ERR_BAD_TABLE;
+      }
+      used[id] = 1;
+    }
+  }
+  return PKV_OK;
+}

@@ -1,0 +1,552 @@
+// Split-KV paged decode: one query per sequence against every cached key.
+//
+// What is computed ([P3] www.mhpn.cn/news/2466452 section 1.1; [P2] "Unlocking
+// long context ..." section 4.1): O = softmax(scale * q K^T) V over the
+// sequence's keys, read page by page through the block table ([P1]
+// "Long-context inference engineering truths 2026 ..." section 2.2; [P2]
+// section 3.1), with kv head h / G serving G query heads ([P3] section 3.2).
+// Each partition of the sequence's blocks keeps the online-softmax state
+// (running max m, running sum l, rescaled accumulator O) of [P1] section 3.1;
+// partitions are combined exactly by the max / log-sum-exp correction of [P4]
+// "Sequence-parallel engineering ..." section "numerically stable incremental
+// softmax" (merge.hip).
+//
+// Decode reads every K/V byte once and does about 4*G flops per byte: it is
+// HBM-bound ([P2] section 5.1).  The MFMA path keeps the arithmetic off the
+// vector ALUs so that the waves spend their issue slots on loads:
+//   S^T[t][g] = K[t][:] . Q[g][:]     v_mfma_f32_16x16x32 (bf16, or f16 for E4M3)
+//   O^T[d][g] += V^T[d][t] P^T[t][g]  v_mfma_f32_16x16x16
+// One wave owns one page (16 tokens) per step.  Lane l holds token 4*(l/16)+i
+// (i < 4) of the page for query head l%16: that is both the output layout of
+// the score product and the B-operand layout of the PV product, so softmax
+// weights never leave their lane.  K pages are token-major ([16][d]); V pages
+// are dimension-major ([d][16]) so each lane's four tokens of one dimension are
+// 8 contiguous bytes (4 for E4M3).
+#include <type_traits>
+
+#include "pkv_common.h"
+
+namespace pkv {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNW = 4;            // waves per workgroup = one partition
+constexpr int kThreads = 64 * kNW;
+
+struct DecodeParams {
+  const uint8_t* k;
+  const uint8_t* v;
+  int64_t block_stride_bytes;
+  const float* k_scale;
+  const float* v_scale;
+  int num_blocks, hkv, hq, G, HG;
+  const void* q;
+  int q_dtype;
+  const int32_t* tables;
+  int maxb;
+  const int32_t* seq_lens;
+  float scale_log2;          // softmax scale * log2(e)
+  int P, PB;
+  float* part_o;             // [B*hq][P][D], unnormalised, relative to part_m
+  float* part_m;             // [B*hq][P], log2 units
+  float* part_l;             // [B*hq][P]
+};
+
+__device__ __forceinline__ int seq_len_clamped(const DecodeParams& p, int b) {
+  int n = p.seq_lens[b];
+  n = n < 0 ? 0 : n;
+  return min(n, p.maxb * kBlock);
+}
+
+template <int D>
+struct SoftState {
+  float m;            // running max, log2 units (shared by the 4 lanes of a head)
+  float l;            // this lane's share of the running sum
+  f32x4 o[D / 16];    // O^T[16n + 4*(l/16) + i][head l%16]
+};
+
+// Online-softmax step over this lane's 4 scores x (log2 units, -inf = masked).
+// The max is taken over the 16 tokens of the page (the 4 lanes of one head).
+template <int D>
+__device__ __forceinline__ void online_update(SoftState<D>& st, const float (&x)[4],
+                                              float (&pw)[4]) {
+  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+  st.l = st.l * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
+  if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) st.o[n] *= alpha;
+  }
+  st.m = m_new;
+}
+
+// Number of this lane's 4 tokens (starting at tok) that are below n, as a mask
+// of 16-bit (bf16) or 8-bit (E4M3) lanes.
+__device__ __forceinline__ int valid_count(int tok, int n) {
+  const int c = n - tok;
+  return c < 0 ? 0 : (c > 4 ? 4 : c);
+}
+
+// ---- bf16 pages ---------------------------------------------------------------
+template <int D>
+struct BF16Page {
+  u32x4 k[D / 32];     // K[t = l%16][32c + 8*(l/16) .. +8]
+  u32x2 v[D / 16];     // V^T[16n + l%16][4*(l/16) .. +4]
+};
+
+template <int D>
+__device__ __forceinline__ void load_page(BF16Page<D>& pg, const uint8_t* kp, const uint8_t* vp,
+                                          int col, int grp) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    pg.k[c] = *reinterpret_cast<const u32x4*>(kp + 2 * (col * D + 32 * c + 8 * grp));
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n)
+    pg.v[n] = *reinterpret_cast<const u32x2*>(vp + 2 * ((16 * n + col) * 16 + 4 * grp));
+}
+
+template <int D>
+__device__ __forceinline__ void compute_page(SoftState<D>& st, const BF16Page<D>& pg,
+                                             const u32x4 (&qf)[D / 32], int tok, int n,
+                                             float sl2) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pg.k[c]),
+                                               __builtin_bit_cast(bf16x8, qf[c]), s, 0, 0, 0);
+  const int vc = valid_count(tok, n);
+  float x[4], pw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = i < vc ? s[i] * sl2 : -INFINITY;
+  online_update<D>(st, x, pw);
+  // The weights enter the PV product as a bf16 pair hi + lo (lo = bf16 of the
+  // remainder), so they keep about 16 significant bits: decode has MFMA time
+  // to spare, and one bf16 rounding of a weight alone would cost up to 2^-9
+  // relative on rows with few keys.
+  s16x4 pb_hi, pb_lo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t h = f32_to_bf16_bits(pw[i]);
+    pb_hi[i] = (short)h;
+    pb_lo[i] = (short)f32_to_bf16_bits(pw[i] - bf16_bits_to_f32(h));
+  }
+  // masked tokens: select the V values away (stale slots may hold anything)
+  u32x2 keep = {vc >= 2 ? 0xffffffffu : (vc == 1 ? 0x0000ffffu : 0u),
+                vc >= 4 ? 0xffffffffu : (vc == 3 ? 0x0000ffffu : 0u)};
+#pragma unroll
+  for (int nn = 0; nn < D / 16; ++nn) {
+    const u32x2 vv = pg.v[nn] & keep;
+    st.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb_hi,
+                                                        st.o[nn], 0, 0, 0);
+  }
+#pragma unroll
+  for (int nn = 0; nn < D / 16; ++nn) {
+    const u32x2 vv = pg.v[nn] & keep;
+    st.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb_lo,
+                                                        st.o[nn], 0, 0, 0);
+  }
+}
+
+// ---- E4M3 pages ---------------------------------------------------------------
+template <int D>
+struct FP8Page {
+  u32x2 k[D / 32];     // 8 codes: K[t = l%16][32c + 8*(l/16) .. +8]
+  uint32_t v[D / 16];  // 4 codes: V^T[16n + l%16][4*(l/16) .. +4]
+  float ks, vs;        // scales of this (block, head)
+};
+
+template <int D>
+__device__ __forceinline__ void load_page(FP8Page<D>& pg, const uint8_t* kp, const uint8_t* vp,
+                                          int col, int grp) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    pg.k[c] = *reinterpret_cast<const u32x2*>(kp + col * D + 32 * c + 8 * grp);
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n)
+    pg.v[n] = *reinterpret_cast<const uint32_t*>(vp + (16 * n + col) * 16 + 4 * grp);
+}
+
+__device__ __forceinline__ f16x8 codes8_to_f16(u32x2 c) {
+  u32x4 h = {e4m3x2_to_f16x2_scaled(c.x & 0xffffu), e4m3x2_to_f16x2_scaled(c.x >> 16),
+             e4m3x2_to_f16x2_scaled(c.y & 0xffffu), e4m3x2_to_f16x2_scaled(c.y >> 16)};
+  return __builtin_bit_cast(f16x8, h);
+}
+__device__ __forceinline__ f16x4 codes4_to_f16(uint32_t c) {
+  u32x2 h = {e4m3x2_to_f16x2_scaled(c & 0xffffu), e4m3x2_to_f16x2_scaled(c >> 16)};
+  return __builtin_bit_cast(f16x4, h);
+}
+
+// E4M3 values enter the MFMA as fp16 equal to value * 2^-8; the 2^8 and the
+// per-block scales are applied in fp32 to the scores and to each page's PV
+// product.
+template <int D>
+__device__ __forceinline__ void compute_page(SoftState<D>& st, const FP8Page<D>& pg,
+                                             const u32x4 (&qf)[D / 32], int tok, int n,
+                                             float sl2) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16(pg.k[c]),
+                                              __builtin_bit_cast(f16x8, qf[c]), s, 0, 0, 0);
+  const int vc = valid_count(tok, n);
+  const float kf = sl2 * 256.f * pg.ks;
+  float x[4], pw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = i < vc ? s[i] * kf : -INFINITY;
+  online_update<D>(st, x, pw);
+  f16x4 pb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pb[i] = (_Float16)pw[i];
+  const uint32_t keep = vc >= 4 ? 0xffffffffu : ((1u << (8 * vc)) - 1u);
+  const float vf = 256.f * pg.vs;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nn = 0; nn < D / 16; ++nn) {
+    const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_f16(pg.v[nn] & keep), pb,
+                                                         zero, 0, 0, 0);
+    st.o[nn] += t * vf;
+  }
+}
+
+template <int D, int KVF>
+using PageT = typename std::conditional<KVF == PKV_BF16, BF16Page<D>, FP8Page<D>>::type;
+
+template <int D, int KVF>
+__device__ __forceinline__ bool issue_page(PageT<D, KVF>& pg, const DecodeParams& p, int blk,
+                                           int kvh, int col, int grp) {
+  const bool ok = (unsigned)blk < (unsigned)p.num_blocks;
+  const int64_t base = (int64_t)(ok ? blk : 0) * p.block_stride_bytes;
+  constexpr int esz = KVF == PKV_BF16 ? 2 : 1;
+  const uint8_t* kp = p.k + base + (int64_t)kvh * kBlock * D * esz;
+  const uint8_t* vp = p.v + base + (int64_t)kvh * D * kBlock * esz;
+  load_page<D>(pg, kp, vp, col, grp);
+  if constexpr (KVF == PKV_FP8_E4M3) {
+    const int64_t si = (int64_t)(ok ? blk : 0) * p.hkv + kvh;
+    pg.ks = p.k_scale[si];
+    pg.vs = p.v_scale[si];
+  }
+  return ok;
+}
+
+// grid (P, hkv * HG, B): one workgroup per (partition, kv head, 16-head group,
+// sequence); wave w takes pages w, w+4, ... of the partition, two in flight.
+template <int D, int KVF>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+  __shared__ float sm_o[kNW][16][D];
+  __shared__ float sm_m[kNW][16];
+  __shared__ float sm_l[kNW][16];
+
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y / p.HG;
+  const int hg = blockIdx.y - kvh * p.HG;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int gi = hg * 16 + col;
+  const bool head_ok = gi < p.G;
+  const int n = seq_len_clamped(p, b);
+  const int nblk = (n + kBlock - 1) / kBlock;
+  const int j0 = part * p.PB;
+  const int j1 = min(j0 + p.PB, nblk);
+
+  // query fragment (B operand of the score product): Q[g = col][32c + 8*grp .. +8]
+  u32x4 qf[D / 32];
+  {
+    const uint16_t* qp =
+        reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)b * p.hq + (int64_t)kvh * p.G + gi) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      u32x4 raw = head_ok ? *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * grp)
+                          : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (KVF == PKV_FP8_E4M3) {
+        // bf16 -> fp16 (exact for |q| in fp16's normal range)
+        u32x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const _Float16 lo = (_Float16)bf16_bits_to_f32(raw[e] & 0xffffu);
+          const _Float16 hi = (_Float16)bf16_bits_to_f32(raw[e] >> 16);
+          h[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        raw = h;
+      }
+      qf[c] = raw;
+    }
+  }
+
+  SoftState<D> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int nn = 0; nn < D / 16; ++nn) st.o[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* trow = p.tables + (int64_t)b * p.maxb;
+  const int mine = j1 - j0 - w;
+  const int cnt = mine > 0 ? (mine + kNW - 1) / kNW : 0;
+  // table entries of this wave's pages, 64 at a time: lane i -> page k = base + i
+  auto table_chunk = [&](int base) {
+    const int jj = j0 + w + kNW * (base + lane);
+    return jj < j1 ? trow[jj] : -1;
+  };
+  int tabv = cnt > 0 ? table_chunk(0) : -1;
+  auto blk_of = [&](int k) {
+    if ((k & 63) == 0 && k > 0) tabv = table_chunk(k);
+    return __builtin_amdgcn_readlane(tabv, k & 63);
+  };
+
+  PageT<D, KVF> pa, pb;
+  bool ok_a = false, ok_b = false;
+  if (cnt > 0) ok_a = issue_page<D, KVF>(pa, p, blk_of(0), kvh, col, grp);
+  for (int k = 0; k < cnt; k += 2) {
+    if (k + 1 < cnt) ok_b = issue_page<D, KVF>(pb, p, blk_of(k + 1), kvh, col, grp);
+    if (ok_a)
+      compute_page<D>(st, pa, qf, (j0 + w + kNW * k) * kBlock + 4 * grp, n, p.scale_log2);
+    if (k + 1 >= cnt) break;
+    if (k + 2 < cnt) ok_a = issue_page<D, KVF>(pa, p, blk_of(k + 2), kvh, col, grp);
+    if (ok_b)
+      compute_page<D>(st, pb, qf, (j0 + w + kNW * (k + 1)) * kBlock + 4 * grp, n, p.scale_log2);
+  }
+
+  // wave state -> LDS (sum l over the 4 lanes of each head)
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (grp == 0) {
+    sm_m[w][col] = st.m;
+    sm_l[w][col] = l;
+  }
+#pragma unroll
+  for (int nn = 0; nn < D / 16; ++nn)
+    *reinterpret_cast<f32x4*>(&sm_o[w][col][16 * nn + 4 * grp]) = st.o[nn];
+  __syncthreads();
+
+  // combine the 4 waves: thread -> (head g, D/16 dims)
+  const int g = threadIdx.x >> 4, dc = threadIdx.x & 15;
+  if (hg * 16 + g >= p.G) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < kNW; ++ww) M = fmaxf(M, sm_m[ww][g]);
+  float a[kNW];
+  float L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < kNW; ++ww) {
+    const float mw = sm_m[ww][g];
+    a[ww] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+    L += a[ww] * sm_l[ww][g];
+  }
+  const int64_t row = (int64_t)b * p.hq + (int64_t)kvh * p.G + hg * 16 + g;
+  float* po = p.part_o + (row * p.P + part) * D;
+  constexpr int DPT = D / 16;
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) {
+    const int d = dc * DPT + e;
+    float acc = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kNW; ++ww) acc += a[ww] * sm_o[ww][g][d];
+    po[d] = acc;
+  }
+  if (dc == 0) {
+    p.part_m[row * p.P + part] = M;
+    p.part_l[row * p.P + part] = L;
+  }
+}
+
+// ---- simple path: any supported dtype pair, vector ALU, one wave per
+// (partition, kv head, sequence); heads of the group one after another.
+template <int QT, int KT>
+__device__ __forceinline__ float kv_value(const uint8_t* base, int64_t idx) {
+  if constexpr (KT == PKV_F32) return reinterpret_cast<const float*>(base)[idx];
+  else if constexpr (KT == PKV_BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+  else {
+    const uint32_t c = base[idx];
+    const uint32_t h = ((c & 0x7fu) << 7) | ((c & 0x80u) << 8);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h) * 256.f;
+  }
+}
+
+template <int QT, int KT>
+__global__ __launch_bounds__(64) void decode_simple_kernel(DecodeParams p, int D) {
+  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int n = seq_len_clamped(p, b);
+  const int nblk = (n + kBlock - 1) / kBlock;
+  const int j0 = part * p.PB, j1 = min(j0 + p.PB, nblk);
+  constexpr int esz = KT == PKV_F32 ? 4 : (KT == PKV_BF16 ? 2 : 1);
+  const int32_t* trow = p.tables + (int64_t)b * p.maxb;
+  for (int gi = 0; gi < p.G; ++gi) {
+    const int64_t row = (int64_t)b * p.hq + (int64_t)kvh * p.G + gi;
+    float q[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
+      float val = 0.f;
+      if (d < D) {
+        if constexpr (QT == PKV_F32) val = reinterpret_cast<const float*>(p.q)[row * D + d];
+        else val = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.q)[row * D + d]);
+      }
+      q[e] = val;
+    }
+    float m = -INFINITY, l = 0.f, o[2] = {0.f, 0.f};
+    for (int j = j0; j < j1; ++j) {
+      const int blk = trow[j];
+      if ((unsigned)blk >= (unsigned)p.num_blocks) continue;
+      const uint8_t* kp = p.k + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * kBlock * D * esz;
+      const uint8_t* vp = p.v + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * D * kBlock * esz;
+      float ks = 1.f, vs = 1.f;
+      if constexpr (KT == PKV_FP8_E4M3) {
+        ks = p.k_scale[(int64_t)blk * p.hkv + kvh];
+        vs = p.v_scale[(int64_t)blk * p.hkv + kvh];
+      }
+      for (int t = 0; t < kBlock && j * kBlock + t < n; ++t) {
+        float part_dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int d = lane + 64 * e;
+          if (d < D) part_dot += q[e] * kv_value<QT, KT>(kp, t * D + d);
+        }
+        const float s = wave_sum(part_dot) * ks * p.scale_log2;
+        const float m_new = fmaxf(m, s);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        const float pw = __builtin_amdgcn_exp2f(s - m_new);
+        l = l * alpha + pw;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int d = lane + 64 * e;
+          const float vv = d < D ? kv_value<QT, KT>(vp, d * kBlock + t) * vs : 0.f;
+          o[e] = o[e] * alpha + pw * vv;
+        }
+        m = m_new;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
+      if (d < D) p.part_o[(row * p.P + part) * D + d] = o[e];
+    }
+    if (lane == 0) {
+      p.part_m[row * p.P + part] = m;
+      p.part_l[row * p.P + part] = l;
+    }
+  }
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int B, int hq, int hkv, int head_dim, int maxb, int partition_blocks,
+                       int q_dtype, int kv_dtype) {
+  DecodePlan plan{};
+  plan.mfma = q_dtype == PKV_BF16 && (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3);
+  const int G = hq / hkv;
+  plan.head_groups = plan.mfma ? (G + 15) / 16 : 1;
+  int pb = partition_blocks;
+  if (pb <= 0) {
+    // enough workgroups to fill 256 CUs several times over
+    const int64_t units = (int64_t)B * hkv * plan.head_groups;
+    const int64_t target = plan.mfma ? 1024 : 2048;
+    int64_t P = units > 0 ? (target + units - 1) / units : 1;
+    if (P < 1) P = 1;
+    if (P > maxb) P = maxb;
+    pb = (int)((maxb + P - 1) / P);
+    if (pb < 1) pb = 1;
+  }
+  plan.partition_blocks = pb;
+  plan.partitions = (maxb + pb - 1) / pb;
+  if (plan.partitions < 1) plan.partitions = 1;
+  const size_t rows = (size_t)B * hq * plan.partitions;
+  size_t bytes = rows * head_dim * sizeof(float);
+  bytes = (bytes + 255) & ~size_t(255);
+  bytes += 2 * ((rows * sizeof(float) + 255) & ~size_t(255));
+  plan.ws_bytes = bytes;
+  return plan;
+}
+
+hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, int hq,
+                         const int32_t* tables, int maxb, const int32_t* seq_lens, float scale,
+                         const DecodePlan& plan, void* out, float* out_lse, void* ws,
+                         hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const int D = c.head_dim;
+  const size_t rows = (size_t)B * hq * plan.partitions;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  float* part_o = reinterpret_cast<float*>(w);
+  size_t off = (rows * D * sizeof(float) + 255) & ~size_t(255);
+  float* part_m = reinterpret_cast<float*>(w + off);
+  off += (rows * sizeof(float) + 255) & ~size_t(255);
+  float* part_l = reinterpret_cast<float*>(w + off);
+
+  const int esz = c.kv_dtype == PKV_F32 ? 4 : (c.kv_dtype == PKV_BF16 ? 2 : 1);
+  DecodeParams p{};
+  p.k = static_cast<const uint8_t*>(c.k);
+  p.v = static_cast<const uint8_t*>(c.v);
+  p.block_stride_bytes = c.block_stride * esz;
+  p.k_scale = c.k_scale;
+  p.v_scale = c.v_scale;
+  p.num_blocks = c.num_blocks;
+  p.hkv = c.hkv;
+  p.hq = hq;
+  p.G = hq / c.hkv;
+  p.HG = plan.head_groups;
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.tables = tables;
+  p.maxb = maxb;
+  p.seq_lens = seq_lens;
+  p.scale_log2 = scale * kLog2e;
+  p.P = plan.partitions;
+  p.PB = plan.partition_blocks;
+  p.part_o = part_o;
+  p.part_m = part_m;
+  p.part_l = part_l;
+
+  if (plan.mfma) {
+    dim3 grid(plan.partitions, c.hkv * plan.head_groups, B), block(kThreads);
+    if (c.kv_dtype == PKV_BF16) {
+      if (D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, PKV_BF16>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((decode_mfma_kernel<64, PKV_BF16>), grid, block, 0, s, p);
+    } else {
+      if (D == 128) hipLaunchKernelGGL((decode_mfma_kernel<128, PKV_FP8_E4M3>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((decode_mfma_kernel<64, PKV_FP8_E4M3>), grid, block, 0, s, p);
+    }
+  } else {
+    dim3 grid(plan.partitions, c.hkv, B), block(64);
+    if (q_dtype == PKV_F32) {
+      if (c.kv_dtype == PKV_F32) hipLaunchKernelGGL((decode_simple_kernel<PKV_F32, PKV_F32>), grid, block, 0, s, p, D);
+      else if (c.kv_dtype == PKV_BF16) hipLaunchKernelGGL((decode_simple_kernel<PKV_F32, PKV_BF16>), grid, block, 0, s, p, D);
+      else return hipErrorInvalidValue;
+    } else {
+      if (c.kv_dtype == PKV_F32) hipLaunchKernelGGL((decode_simple_kernel<PKV_BF16, PKV_F32>), grid, block, 0, s, p, D);
+      else return hipErrorInvalidValue;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  MergeArgs a{};
+  a.S = plan.partitions;
+  a.rows = (int64_t)B * hq;
+  a.D = D;
+  a.o = part_o;
+  a.o_row = (int64_t)plan.partitions * D;
+  a.o_part = D;
+  a.m = part_m;
+  a.l = part_l;
+  a.ml_row = plan.partitions;
+  a.ml_part = 1;
+  a.m_log2 = true;
+  a.out = out;
+  a.out_dtype = q_dtype;
+  a.out_m = nullptr;
+  a.out_l = nullptr;
+  a.out_lse = out_lse;
+  return launch_merge(a, s);
+}
+
+}  // namespace pkv

@@ -1,0 +1,171 @@
+// kv_append (reshape-and-cache) and FP8 block-wise scales.
+//
+// [P1] "Long-context inference engineering truths 2026 ..." section 2.2: a
+// token at position t lands in slot t % 16 of the physical block that the
+// sequence's table names for logical block t / 16.
+// [P2] "Unlocking long context ..." section 3.2: FP8 (E4M3) KV with one scale
+// per group of 64-128 tokens (64 here).
+#include "pkv_common.h"
+
+namespace pkv {
+namespace {
+
+struct AppendParams {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  int64_t block_stride;      // elements
+  const float* k_scale;
+  const float* v_scale;
+  int num_blocks, hkv, D;
+  const void* k_new;
+  const void* v_new;
+  int num_tokens;
+  const int32_t* seq_idx;
+  const int32_t* pos;
+  const int32_t* tables;
+  int num_seqs, maxb;
+};
+
+template <typename T>
+__device__ __forceinline__ T load_elem(const void* p, int64_t i) {
+  return reinterpret_cast<const T*>(p)[i];
+}
+
+// One wave per token, four tokens per 256-thread workgroup.  Same-type caches
+// copy raw bits; E4M3 caches quantise f32(x) * f32(1/scale) of the block.
+template <int SRC, int DST>
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= p.num_tokens) return;
+  const int b = p.seq_idx[tok];
+  const int pos = p.pos[tok];
+  if (b < 0 || b >= p.num_seqs || pos < 0 || (pos >> 4) >= p.maxb) return;
+  const int blk = p.tables[(int64_t)b * p.maxb + (pos >> 4)];
+  if (blk < 0 || blk >= p.num_blocks) return;
+  const int off = pos & (kBlock - 1);
+  const int HD = p.hkv * p.D;
+  const int64_t src0 = (int64_t)tok * HD;
+  const int64_t base = (int64_t)blk * p.block_stride;
+  for (int e = lane; e < HD; e += 64) {
+    const int h = e / p.D;
+    const int d = e - h * p.D;
+    const int64_t kd = base + (int64_t)h * kBlock * p.D + (int64_t)off * p.D + d;
+    const int64_t vd = base + (int64_t)h * p.D * kBlock + (int64_t)d * kBlock + off;
+    if constexpr (DST == PKV_FP8_E4M3) {
+      float xk, xv;
+      if constexpr (SRC == PKV_BF16) {
+        xk = bf16_bits_to_f32(load_elem<uint16_t>(p.k_new, src0 + e));
+        xv = bf16_bits_to_f32(load_elem<uint16_t>(p.v_new, src0 + e));
+      } else {
+        xk = load_elem<float>(p.k_new, src0 + e);
+        xv = load_elem<float>(p.v_new, src0 + e);
+      }
+      const float inv_k = __frcp_rn(p.k_scale[(int64_t)blk * p.hkv + h]);
+      const float inv_v = __frcp_rn(p.v_scale[(int64_t)blk * p.hkv + h]);
+      p.k_pool[kd] = (uint8_t)e4m3_encode(__fmul_rn(xk, inv_k));
+      p.v_pool[vd] = (uint8_t)e4m3_encode(__fmul_rn(xv, inv_v));
+    } else if constexpr (DST == PKV_BF16) {
+      reinterpret_cast<uint16_t*>(p.k_pool)[kd] = load_elem<uint16_t>(p.k_new, src0 + e);
+      reinterpret_cast<uint16_t*>(p.v_pool)[vd] = load_elem<uint16_t>(p.v_new, src0 + e);
+    } else {
+      reinterpret_cast<float*>(p.k_pool)[kd] = load_elem<float>(p.k_new, src0 + e);
+      reinterpret_cast<float*>(p.v_pool)[vd] = load_elem<float>(p.v_new, src0 + e);
+    }
+  }
+}
+
+struct ScaleParams {
+  float* k_scale;
+  float* v_scale;
+  int hkv, D, num_blocks;
+  const void* k_src;
+  const void* v_src;
+  int num_tokens, pos0;
+  const int32_t* table_row;
+  int maxb;
+};
+
+template <int SRC>
+__device__ __forceinline__ float src_abs(const void* p, int64_t i) {
+  if constexpr (SRC == PKV_BF16) return fabsf(bf16_bits_to_f32(load_elem<uint16_t>(p, i)));
+  else return fabsf(load_elem<float>(p, i));
+}
+
+// grid (groups, hkv): largest magnitude over a 64-token group for one head,
+// for K and V; scale = f32(amax / 448), 1 if that is 0 or subnormal.
+template <int SRC>
+__global__ __launch_bounds__(256) void fp8_scale_kernel(ScaleParams p) {
+  __shared__ float red[2][4];
+  const int g = blockIdx.x, h = blockIdx.y;
+  const int t0 = g * kScaleGroup;
+  const int t1 = min(t0 + kScaleGroup, p.num_tokens);
+  float ak = 0.f, av = 0.f;
+  const int n = (t1 - t0) * p.D;
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int t = t0 + e / p.D, d = e % p.D;
+    const int64_t i = ((int64_t)t * p.hkv + h) * p.D + d;
+    ak = fmaxf(ak, src_abs<SRC>(p.k_src, i));
+    av = fmaxf(av, src_abs<SRC>(p.v_src, i));
+  }
+  ak = wave_max(ak);
+  av = wave_max(av);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][w] = ak; red[1][w] = av; }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  ak = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  av = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  float sk = __fdiv_rn(ak, 448.0f);
+  float sv = __fdiv_rn(av, 448.0f);
+  if (!(sk >= 1.17549435e-38f)) sk = 1.0f;
+  if (!(sv >= 1.17549435e-38f)) sv = 1.0f;
+  const int first = p.pos0 + t0, last = p.pos0 + t1 - 1;
+  for (int j = first / kBlock; j <= last / kBlock && j < p.maxb; ++j) {
+    const int blk = p.table_row[j];
+    if (blk < 0 || blk >= p.num_blocks) continue;
+    p.k_scale[(int64_t)blk * p.hkv + h] = sk;
+    p.v_scale[(int64_t)blk * p.hkv + h] = sv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const CacheView& c, void* k_pool, void* v_pool, const void* k_new,
+                            const void* v_new, int src_dtype, int num_tokens,
+                            const int32_t* seq_idx, const int32_t* pos, const int32_t* tables,
+                            int num_seqs, int maxb, hipStream_t s) {
+  if (num_tokens == 0) return hipSuccess;
+  AppendParams p{static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), c.block_stride,
+                 c.k_scale, c.v_scale, c.num_blocks, c.hkv, c.head_dim, k_new, v_new,
+                 num_tokens, seq_idx, pos, tables, num_seqs, maxb};
+  dim3 grid((num_tokens + 3) / 4), block(256);
+  if (c.kv_dtype == PKV_FP8_E4M3) {
+    if (src_dtype == PKV_BF16)
+      hipLaunchKernelGGL((kv_append_kernel<PKV_BF16, PKV_FP8_E4M3>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((kv_append_kernel<PKV_F32, PKV_FP8_E4M3>), grid, block, 0, s, p);
+  } else if (c.kv_dtype == PKV_BF16) {
+    hipLaunchKernelGGL((kv_append_kernel<PKV_BF16, PKV_BF16>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((kv_append_kernel<PKV_F32, PKV_F32>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_group_scales(const CacheView& c, float* k_scale, float* v_scale,
+                                   const void* k_src, const void* v_src, int src_dtype,
+                                   int num_tokens, int pos0, const int32_t* table_row,
+                                   int maxb, hipStream_t s) {
+  if (num_tokens == 0) return hipSuccess;
+  ScaleParams p{k_scale, v_scale, c.hkv, c.head_dim, c.num_blocks, k_src, v_src,
+                num_tokens, pos0, table_row, maxb};
+  dim3 grid((num_tokens + kScaleGroup - 1) / kScaleGroup, c.hkv), block(256);
+  if (src_dtype == PKV_BF16)
+    hipLaunchKernelGGL(fp8_scale_kernel<PKV_BF16>, grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL(fp8_scale_kernel<PKV_F32>, grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

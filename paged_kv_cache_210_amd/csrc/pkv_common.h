@@ -1,0 +1,141 @@
+// Internal helpers shared by the libpkv kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+constexpr int kBlock = PKV_BLOCK_SIZE;   // tokens per physical block
+constexpr int kScaleGroup = PKV_SCALE_GROUP;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- element conversions ---------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// OCP E4M3FN encode of an fp32 value: round to nearest, ties to the even
+// mantissa; magnitudes at or beyond 448 saturate to 448; NaN gives 0x7F.
+// Integer arithmetic only, so host and device agree bit for bit.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                  // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;          // >= 448 (incl. inf)
+  if (a < 0x3c800000u) {                              // below 2^-6: subnormal grid
+    // steps of 2^-9; the scaling by 2^9 is exact, rintf rounds ties to even.
+    const float q = rintf(__uint_as_float(a) * 512.0f);
+    return sign | (uint32_t)q;                        // q == 8 is the smallest normal
+  }
+  const uint32_t e = (a >> 23) - 127u + 7u;           // biased E4M3 exponent, 1..15
+  const uint32_t keep = (a >> 20) & 0x7u;
+  const uint32_t rem = a & 0xfffffu;
+  uint32_t code = (e << 3) | keep;
+  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) code += 1u;
+  if (code > 0x7eu) code = 0x7eu;
+  return sign | code;
+}
+
+// E4M3 byte -> fp16 bit pattern whose value is the E4M3 value times 2^-8.
+// Exact for every finite code, subnormals included (fp16 has one more
+// exponent bit and the bias differs by 8).
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2_scaled(uint32_t two_bytes) {
+  // two_bytes: byte0 in bits 0..7, byte1 in bits 8..15 -> fp16 in halves 0, 1
+  const uint32_t lo = ((two_bytes & 0x7fu) << 7) | ((two_bytes & 0x80u) << 8);
+  const uint32_t hi = ((two_bytes & 0x7f00u) << 15) | ((two_bytes & 0x8000u) << 16);
+  return lo | hi;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+}  // namespace pkv
+
+// Launchers (defined in the .hip files, called by the C ABI in api.cpp).
+namespace pkv {
+struct CacheView {
+  const void* k;
+  const void* v;
+  int64_t block_stride;   // elements
+  const float* k_scale;
+  const float* v_scale;
+  int num_blocks;
+  int hkv;
+  int head_dim;
+  int kv_dtype;
+};
+
+hipError_t launch_kv_append(const CacheView& c, void* k_pool, void* v_pool, const void* k_new,
+                            const void* v_new, int src_dtype, int num_tokens,
+                            const int32_t* seq_idx, const int32_t* pos, const int32_t* tables,
+                            int num_seqs, int maxb, hipStream_t s);
+hipError_t launch_fp8_group_scales(const CacheView& c, float* k_scale, float* v_scale,
+                                   const void* k_src, const void* v_src, int src_dtype,
+                                   int num_tokens, int pos0, const int32_t* table_row,
+                                   int maxb, hipStream_t s);
+
+struct DecodePlan {
+  int partitions;        // P
+  int partition_blocks;  // PB
+  int head_groups;       // ceil(G / 16) for the MFMA path, 1 otherwise
+  bool mfma;
+  size_t ws_bytes;
+};
+DecodePlan plan_decode(int B, int hq, int hkv, int head_dim, int maxb, int partition_blocks,
+                       int q_dtype, int kv_dtype);
+hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, int hq,
+                         const int32_t* tables, int maxb, const int32_t* seq_lens, float scale,
+                         const DecodePlan& plan, void* out, float* out_lse, void* ws,
+                         hipStream_t s);
+
+hipError_t launch_prefill(const CacheView& c, const void* q, int T, int hq, int q_pos0,
+                          const int32_t* table, int maxb, int kv_begin, int kv_end, int causal,
+                          float scale, void* out, float* out_lse, float* part_o, float* part_m,
+                          float* part_l, hipStream_t s);
+
+// Generic strided merge of S partial states per row.
+struct MergeArgs {
+  int S;
+  int64_t rows;
+  int D;
+  const float* o;      // O~ of part s, row r at o + r*o_row + s*o_part
+  int64_t o_row, o_part;
+  const float* m;      // m of part s, row r at m + r*ml_row + s*ml_part
+  const float* l;
+  int64_t ml_row, ml_part;
+  bool m_log2;         // m stored in log2 units (internal decode partials)
+  void* out;
+  int out_dtype;
+  float* out_m;
+  float* out_l;
+  float* out_lse;
+};
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace pkv

@@ -1,0 +1,168 @@
+"""GPU parity of chunked causal prefill and the shard merge through the C ABI,
+against the fp64 oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pkv_oracle as O
+import synth
+from tests._util import bits, compare_rows, oracle_cache
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_cache_210_amd import lib as L
+    L.load()
+    return L
+
+
+def _prompt(lib, n, hq=8, hkv=2, seed=0, pool=None, poison=True, perm_seed=None, device="cpu"):
+    """A one-sequence prompt of n tokens appended into a poisoned pool."""
+    cfg = synth.prefill_config("prefill", n, 4096, 8192, hq, hkv, 128, seed_index=50 + seed,
+                               pool_blocks=pool)
+    if perm_seed is not None:
+        cfg = cfg.with_(perm_seed=perm_seed)
+    inp = synth.prefill_inputs(cfg, device=device)
+    tables, _ = lib.build_tables([n], cfg.pool_blocks, inp["free_order"])
+    td = tables.to(DEV)
+    cache = lib.PagedCache.empty(cfg.pool_blocks, hkv, 128, "bf16",
+                                 fill=float("nan") if poison else None)
+    seq_idx = torch.zeros(n, dtype=torch.int32, device=DEV)
+    pos = torch.arange(n, dtype=torch.int32, device=DEV)
+    lib.kv_append(cache, inp["k"].to(DEV), inp["v"].to(DEV), seq_idx, pos, td)
+    return cfg, inp, tables.numpy(), td, cache
+
+
+def _oracle(cfg, inp, tables, hkv, heads=None):
+    dcfg = synth.decode_config("o", (cfg.prompt_len,), cfg.hq, hkv, 128, pool_blocks=cfg.pool_blocks)
+    return oracle_cache(dcfg, {"k": inp["k"], "v": inp["v"]}, tables, heads=heads)
+
+
+@pytest.mark.parametrize("T,q_pos0,kv_begin,kv_end,causal,scale", [
+    (200, 0, 0, 200, True, 0.0),          # whole prompt, ragged tail
+    (130, 300, 0, 430, True, 0.0),        # a later chunk against everything before it
+    (130, 300, 100, 357, True, 0.0),      # unaligned shard: rows before 100 see nothing
+    (64, 0, 0, 64, True, 0.0),            # one tile
+    (1, 77, 0, 78, True, 0.0),            # a single row
+    (150, 10, 0, 400, False, 0.0),        # non-causal
+    (100, 50, 0, 150, True, 0.3),         # explicit scale
+    (100, 50, 0, 150, True, -0.05),       # negative scale
+])
+def test_prefill_final_matches_oracle(lib, T, q_pos0, kv_begin, kv_end, causal, scale):
+    n = max(kv_end, q_pos0 + T)
+    cfg, inp, tables, td, cache = _prompt(lib, n)
+    q = inp["q"][q_pos0:q_pos0 + T].contiguous()
+    out, lse = lib.paged_attn_prefill(cache, q.to(DEV), q_pos0, td[0], kv_begin, kv_end, causal,
+                                      scale=scale)
+    torch.cuda.synchronize()
+    oc = _oracle(cfg, inp, tables, 2)
+    ref = O.prefill(oc, bits(q), "bf16", q_pos0, tables[0], kv_begin, kv_end, causal,
+                    scale=None if scale == 0.0 else scale)
+    compare_rows(out.float().cpu().numpy(), ref["o"], "bf16", f"prefill {T}@{q_pos0}")
+    gl = lse.cpu().double().numpy()
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.abs(gl[fin] - ref["lse"][fin]).max(initial=0) < 2e-3
+
+
+def test_prefill_partial_matches_oracle_state(lib):
+    n = 500
+    cfg, inp, tables, td, cache = _prompt(lib, n, hq=16, hkv=4, seed=1)
+    q = inp["q"][300:428].contiguous()
+    po, pm, pl = lib.paged_attn_prefill(cache, q.to(DEV), 300, td[0], 37, 333, True, partial=True)
+    torch.cuda.synchronize()
+    oc = _oracle(cfg, inp, tables, 4)
+    ref = O.prefill(oc, bits(q), "bf16", 300, tables[0], 37, 333, True)
+    # compare normalised values and the log-sum-exp (m and l individually are
+    # defined only up to the max shift, which both sides take exactly)
+    gm, gl = pm.cpu().double().numpy(), pl.cpu().double().numpy()
+    np.testing.assert_allclose(gm, ref["m"], rtol=0, atol=1e-5)
+    np.testing.assert_allclose(gl, ref["l"], rtol=2e-3)
+    on = po.cpu().double().numpy() / gl[..., None]
+    compare_rows(on, ref["o"], "bf16", "partial O~/l", out_fmt="f32")
+
+
+def test_shards_merged_equal_whole(lib):
+    """Chunk attention over 3 KV shards + lse merge == one call over all keys."""
+    n, q0, T = 1000, 800, 200
+    cfg, inp, tables, td, cache = _prompt(lib, n, hq=16, hkv=2, seed=2)
+    q = inp["q"][q0:q0 + T].contiguous().to(DEV)
+    whole, wl = lib.paged_attn_prefill(cache, q, q0, td[0], 0, n, True)
+    parts = [lib.paged_attn_prefill(cache, q, q0, td[0], a, b, True, partial=True)
+             for a, b in ((0, 333), (333, 800), (800, 1000))]
+    po = torch.stack([p[0] for p in parts])
+    pm = torch.stack([p[1] for p in parts])
+    pl = torch.stack([p[2] for p in parts])
+    merged, M, L, lse = lib.attn_lse_merge(po, pm, pl, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    oc = _oracle(cfg, inp, tables, 2)
+    ref = O.prefill(oc, bits(q.cpu()), "bf16", q0, tables[0], 0, n, True)
+    compare_rows(merged.float().cpu().numpy(), ref["o"], "bf16", "merged shards")
+    compare_rows(whole.float().cpu().numpy(), ref["o"], "bf16", "whole")
+    fin = np.isfinite(ref["lse"])
+    assert np.abs(lse.cpu().double().numpy()[fin] - ref["lse"][fin]).max() < 2e-3
+
+
+def test_prefill_permutation_bitwise_and_rerun(lib):
+    n = 300
+    outs = []
+    for ps in (None, 4242):
+        cfg, inp, tables, td, cache = _prompt(lib, n, seed=3, perm_seed=ps)
+        q = inp["q"][100:300].contiguous().to(DEV)
+        o1, _ = lib.paged_attn_prefill(cache, q, 100, td[0], 0, n, True)
+        o2, _ = lib.paged_attn_prefill(cache, q, 100, td[0], 0, n, True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        outs.append(o1)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_prefill_row_equals_decode(lib):
+    n = 257
+    cfg, inp, tables, td, cache = _prompt(lib, n, hq=8, hkv=2, seed=4)
+    q = inp["q"][:n].contiguous().to(DEV)
+    pre, _ = lib.paged_attn_prefill(cache, q, 0, td[0], 0, n, True)
+    for p in (0, 15, 16, 100, 256):
+        lens = torch.tensor([p + 1], dtype=torch.int32, device=DEV)
+        dec, _ = lib.paged_attn_decode(cache, q[p:p + 1].contiguous(), td, lens)
+        torch.cuda.synchronize()
+        diff = (pre[p].float() - dec[0].float()).abs().max().item()
+        assert diff <= 8e-3, (p, diff)       # two bf16 roundings of the same value
+
+
+def test_chunked_prefill_c4_sampled(lib):
+    """The 32768-token prompt in 4096-token chunks, KV in 4 sequential 8192-token
+    shards merged by LSE, as the whole-prompt flow runs it; sampled rows are
+    checked against the oracle."""
+    cfg = synth.CONFIGS["C4"]
+    inp = synth.prefill_inputs(cfg, device=DEV)
+    tables, _ = lib.build_tables([cfg.prompt_len], cfg.pool_blocks, inp["free_order"])
+    td = tables.to(DEV)
+    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, 128, "bf16", fill=float("nan"))
+    outs = torch.empty_like(inp["q"])
+    C, S = cfg.chunk, cfg.shard_len
+    for c in range(cfg.num_chunks):
+        a, b = c * C, (c + 1) * C
+        lib.kv_append(cache, inp["k"][a:b], inp["v"][a:b],
+                      torch.zeros(C, dtype=torch.int32, device=DEV),
+                      torch.arange(a, b, dtype=torch.int32, device=DEV), td)
+        q = inp["q"][a:b]
+        shards = [(j * S, min((j + 1) * S, b)) for j in range(b // S + (1 if b % S else 0))]
+        parts = [lib.paged_attn_prefill(cache, q, a, td[0], s0, s1, True, partial=True)
+                 for s0, s1 in shards]
+        lib.attn_lse_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]),
+                           torch.stack([p[2] for p in parts]), out=outs[a:b], with_state=False)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 4095, 4096, 8191, 8192, 16000, 24575, 30001, 32767])
+    tab = tables.numpy()
+    dcfg = synth.decode_config("o", (cfg.prompt_len,), cfg.hq, cfg.hkv, 128,
+                               pool_blocks=cfg.pool_blocks)
+    oc = oracle_cache(dcfg, {"k": inp["k"], "v": inp["v"]}, tab)
+    qs = bits(inp["q"][torch.from_numpy(rows).to(DEV)])
+    got = outs[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    for i, r in enumerate(rows):
+        ref = O.prefill(oc, qs[i:i + 1], "bf16", int(r), tab[0], 0, int(r) + 1, True)
+        compare_rows(got[i:i + 1], ref["o"], "bf16", f"C4 row {r}")
