@@ -64,55 +64,64 @@ def _decode_setup(cfg, partition_blocks):
     }
     q = inp["q"]
     lens = torch.tensor(lens_l, dtype=torch.int32, device=dev)
-    ws = lib.decode_workspace(cache, q, td, partition_blocks)
+    P = lib.decode_partitions(cache, q.dtype, cfg.batch, cfg.hq, td.shape[1], partition_blocks)
+    part = (torch.empty(P, cfg.batch, cfg.hq, cfg.head_dim, dtype=torch.float32, device=dev),
+            torch.empty(P, cfg.batch, cfg.hq, dtype=torch.float32, device=dev),
+            torch.empty(P, cfg.batch, cfg.hq, dtype=torch.float32, device=dev))
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
     del inp, keep
     torch.cuda.synchronize()
-    return dict(cache=cache, td=td, q=q, lens=lens, ws=ws, out=out, lse=lse, step_in=step_in,
-                tables=tables)
+    return dict(cache=cache, td=td, q=q, lens=lens, part=part, out=out, lse=lse,
+                step_in=step_in, tables=tables, partitions=P)
 
 
 def bench_decode(cfg, steps, warmup, partition_blocks=0):
-    """Returns (ms per step, ms per decode call, state)."""
+    """Returns (ms per step, ms per split-KV decode kernel, ms per merge, state).
+
+    A step is pkv_kv_append + pkv_paged_attn_decode_partial + pkv_attn_lse_merge,
+    the two launches pkv_paged_attn_decode makes, with events between them so
+    the dominant kernel is timed on its own."""
     import torch
     from paged_kv_cache_210_amd import lib
 
     st = _decode_setup(cfg, partition_blocks)
     s = st["step_in"]
+    po, pm, pl = st["part"]
 
-    def step(ev0=None, ev1=None):
+    def step(ev=None):
         lib.kv_append(st["cache"], s["k"], s["v"], s["seq"], s["pos"], st["td"])
-        if ev0 is not None:
-            ev0.record()
-        lib.paged_attn_decode(st["cache"], st["q"], st["td"], st["lens"],
-                              partition_blocks=partition_blocks, out=st["out"],
-                              out_lse=st["lse"], ws=st["ws"])
-        if ev1 is not None:
-            ev1.record()
+        if ev is not None:
+            ev[0].record()
+        lib.paged_attn_decode_partial(st["cache"], st["q"], st["td"], st["lens"],
+                                      partition_blocks=partition_blocks, part=st["part"])
+        if ev is not None:
+            ev[1].record()
+        lib.attn_lse_merge(po, pm, pl, out=st["out"], with_state=False, out_lse=st["lse"])
+        if ev is not None:
+            ev[2].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        step(e0[i], e1[i])
+        step(evs[i])
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / steps
-    dec = sorted(e0[i].elapsed_time(e1[i]) for i in range(steps))
-    ms_dec = sum(dec) / len(dec)
-    return ms_step, ms_dec, st
+    ms_dec = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    ms_merge = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    return ms_step, ms_dec, ms_merge, st
 
 
 def decode_record(cfg, steps, warmup, partition_blocks):
     from paged_kv_cache_210_amd import accounting as A
 
-    ms_step, ms_dec, st = bench_decode(cfg, steps, warmup, partition_blocks)
+    ms_step, ms_dec, ms_merge, st = bench_decode(cfg, steps, warmup, partition_blocks)
     kbytes = A.decode_kernel_bytes(cfg.seq_lens, cfg.hq, cfg.hkv, cfg.head_dim, cfg.q_dtype,
                                    cfg.kv_dtype)
     step_bytes = A.decode_step_bytes(cfg.seq_lens, cfg.hq, cfg.hkv, cfg.head_dim, cfg.q_dtype,
@@ -123,12 +132,32 @@ def decode_record(cfg, steps, warmup, partition_blocks):
         "tok_per_s": cfg.batch / (ms_step * 1e-3),
         "ms_per_step": ms_step,
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+        "merge_ms": ms_merge,
+        "partitions": st["partitions"],
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / A.HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "pkv_paged_attn_decode (split-KV partial + LSE merge)",
+                     "frac": gbs / A.HBM_PEAK_GBS, "traffic": measured_traffic(cfg),
+                     "kernel": "decode_mfma_kernel (pkv_paged_attn_decode_partial)",
                      "ms_per_launch": ms_dec, "bytes_per_launch": kbytes},
     }
     return rec, st
+
+
+def measured_traffic(cfg):
+    """HBM bytes per launch of the decode kernel from the committed counter
+    runs (profiles/decode_hbm_traffic.json), or None when the kernel source has
+    changed since they were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "decode_hbm_traffic.json")
+    src = os.path.join(ROOT, "paged_kv_cache_210_amd", "csrc", "decode.hip")
+    key = {"C2": "C2", "C3": "C3", "C5": "C5"}.get(cfg.name.split()[0])
+    try:
+        rec = json.load(open(path))
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha256"]:
+            return None
+        return rec["workloads"][key]["traffic_bytes"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def _prefill_setup(cfg):
@@ -224,6 +253,28 @@ def prefill_record(cfg, reps):
     }
 
 
+def hbm_copy_record(reps=20, nbytes=1 << 30):
+    """A plain device-to-device copy of a known size: the attainable-bandwidth
+    context for the decode roofline, and the reference kernel for scaling the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    return {"workload": f"device copy of {nbytes} bytes", "bytes_read": nbytes,
+            "bytes_written": nbytes, "ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline_decode(cfg, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample of the same decode
     step: append the newest token of each sampled sequence, then attention over
@@ -277,7 +328,7 @@ def main(argv=None):
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["C2", "C3", "C5", "C4", "C4_128K"],
+    ap.add_argument("--only", choices=["C2", "C3", "C5", "C4", "C4_128K", "hbm_copy"],
                     help="run one workload and print its record (for profiling)")
     ap.add_argument("--prefill-reps", type=int, default=2)
     args = ap.parse_args(argv)
@@ -292,6 +343,9 @@ def main(argv=None):
 
     lib.load()
     torch.cuda.init()
+    if args.only == "hbm_copy":
+        print(json.dumps(hbm_copy_record(args.steps)), flush=True)
+        return 0
     if args.only:
         c = synth.CONFIGS[args.only]
         _log(f"[bench] only {c.name}")
@@ -328,6 +382,9 @@ def main(argv=None):
             secondary.append(rec)
             _log(f"[bench]   {rec['tflops']:.0f} TFLOP/s, {rec['ms_per_prompt']:.2f} ms/prompt")
 
+    copy = hbm_copy_record()
+    _log(f"[bench] plain device copy: {copy['gbs']:.0f} GB/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         _log("[bench] cpu baseline (fp64 oracle)")
@@ -351,6 +408,7 @@ def main(argv=None):
                    "block_size": 16, "kv_dtype": cfg.kv_dtype, "pool_blocks": cfg.pool_blocks,
                    "step": "kv_append(1 token/seq) + split-KV decode + LSE merge"},
         "decode_hbm_gbs": head["roofline"]["achieved"],
+        "hbm_copy_gbs": copy["gbs"],
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "secondary": secondary,

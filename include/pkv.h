@@ -132,7 +132,8 @@ void pkv_allocator_destroy(pkv_allocator* a);
  * For token i < num_tokens: block = block_tables[seq_idx[i]*max_blocks_per_seq
  * + pos[i]/16], slot = pos[i]%16; K page row `slot` <- k_new[i][h][:] and V
  * page column `slot` <- v_new[i][h][:] for every kv head h.
- * k_new, v_new: device [num_tokens][num_kv_heads][head_dim], src_dtype.
+ * k_new, v_new: device [num_tokens][num_kv_heads][head_dim], src_dtype,
+ * 16-byte aligned.
  * seq_idx, pos: device int32 [num_tokens]; block_tables: device int32
  * [num_seqs][max_blocks_per_seq].
  * Same-type caches copy bits (src_dtype must equal kv_dtype).  E4M3 caches
@@ -177,9 +178,10 @@ int32_t pkv_fp8_group_scales(const pkv_cache_desc* cache, const void* k_src, con
  * scale == 0 means 1/sqrt(head_dim).  Requires num_q_heads % num_kv_heads == 0.
  * E4M3 caches need q_dtype PKV_BF16.  ws: device buffer of at least
  * pkv_decode_workspace_bytes(cache, q_dtype, B, num_q_heads,
- * max_blocks_per_seq, partition_blocks) bytes, 256-byte aligned; it holds
- * fp32 partials only, needs no initialisation, and may be reused by the
- * next call once this one has finished on the stream. */
+ * max_blocks_per_seq, partition_blocks) bytes, 256-byte aligned, holding
+ * the fp32 partials only; it needs no initialisation and may be reused by
+ * the next call once this one has finished on the stream.  Calls that
+ * overlap on one workspace race. */
 int32_t pkv_decode_workspace_bytes(const pkv_cache_desc* cache, int32_t q_dtype, int32_t B,
                                    int32_t num_q_heads, int32_t max_blocks_per_seq,
                                    int32_t partition_blocks, size_t* bytes);
@@ -188,6 +190,27 @@ int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q, int32_
                               int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
                               int32_t partition_blocks, void* out, float* out_lse, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* ---- split-KV decode, partial form [P4 incremental softmax] -------------------
+ * The attention of pkv_paged_attn_decode stopped before the merge, for callers
+ * that merge partitions themselves (e.g. partitions held by several devices).
+ * Partition p covers logical blocks [p*PB, (p+1)*PB) of every sequence, PB =
+ * partition_blocks (0 = the library's choice); the partition count P comes
+ * from pkv_decode_partitions with the same arguments.  Outputs, part-major so
+ * pkv_attn_lse_merge(S = P, rows = B*num_q_heads, ...) merges them directly:
+ *   part_o fp32 [P][B][num_q_heads][head_dim] unnormalised O~,
+ *   part_m fp32 [P][B][num_q_heads] max score (natural units, -inf if the
+ *          partition holds no key of the sequence), part_l fp32 sum of
+ *          exp(score - m) (0 then). */
+int32_t pkv_decode_partitions(const pkv_cache_desc* cache, int32_t q_dtype, int32_t B,
+                              int32_t num_q_heads, int32_t max_blocks_per_seq,
+                              int32_t partition_blocks, int32_t* partitions);
+int32_t pkv_paged_attn_decode_partial(const pkv_cache_desc* cache, const void* q, int32_t q_dtype,
+                                      int32_t B, int32_t num_q_heads,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, float scale,
+                                      int32_t partition_blocks, float* part_o, float* part_m,
+                                      float* part_l, void* stream);
 
 /* ---- chunked causal prefill against paged KV [P2 4.1, P2 5.2, P3 1.2] ----
  * Query rows q[r] (r < T) of one sequence sit at absolute positions q_pos0+r.

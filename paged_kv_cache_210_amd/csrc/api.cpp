@@ -83,6 +83,7 @@ extern "C" int32_t pkv_kv_append(const pkv_cache_desc* cache, const void* k_new,
   }
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !seq_idx || !pos || !block_tables) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_INVALID_ARG;
   return from_hip(pkv::launch_kv_append(view(cache), cache->k_cache, cache->v_cache, k_new, v_new,
                                         src_dtype, num_tokens, seq_idx, pos, block_tables,
                                         num_seqs, max_blocks_per_seq, stream_of(stream)));
@@ -151,6 +152,49 @@ extern "C" int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void
                                      stream_of(stream)));
 }
 
+extern "C" int32_t pkv_decode_partitions(const pkv_cache_desc* cache, int32_t q_dtype,
+                                         int32_t B, int32_t num_q_heads,
+                                         int32_t max_blocks_per_seq, int32_t partition_blocks,
+                                         int32_t* partitions) {
+  int32_t st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (!partitions || B < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
+      partition_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % cache->num_kv_heads) return PKV_ERR_INVALID_ARG;
+  if (q_dtype != PKV_F32 && q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  *partitions = pkv::plan_decode(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                 max_blocks_per_seq, partition_blocks, q_dtype, cache->kv_dtype)
+                    .partitions;
+  return PKV_OK;
+}
+
+extern "C" int32_t pkv_paged_attn_decode_partial(
+    const pkv_cache_desc* cache, const void* q, int32_t q_dtype, int32_t B, int32_t num_q_heads,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
+    int32_t partition_blocks, float* part_o, float* part_m, float* part_l, void* stream) {
+  int32_t st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (q_dtype != PKV_F32 && q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (B < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % cache->num_kv_heads) return PKV_ERR_INVALID_ARG;
+  if (cache->kv_dtype == PKV_FP8_E4M3 && q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  float sc;
+  if (!resolve_scale(scale, cache->head_dim, &sc)) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!q || !block_tables || !seq_lens || !part_o || !part_m || !part_l)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(part_o)) return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  pkv::DecodePlan plan = pkv::plan_decode(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                          max_blocks_per_seq, partition_blocks, q_dtype,
+                                          cache->kv_dtype);
+  return from_hip(pkv::launch_decode_partial(view(cache), q, q_dtype, B, num_q_heads,
+                                             block_tables, max_blocks_per_seq, seq_lens, sc, plan,
+                                             part_o, part_m, part_l, stream_of(stream)));
+}
+
 extern "C" int32_t pkv_paged_attn_prefill(const pkv_cache_desc* cache, const void* q,
                                           int32_t q_dtype, int32_t T, int32_t num_q_heads,
                                           int32_t q_pos0, const int32_t* block_table,
@@ -202,7 +246,6 @@ extern "C" int32_t pkv_attn_lse_merge(int32_t S, int64_t rows, int32_t head_dim,
   a.l = part_l;
   a.ml_row = 1;
   a.ml_part = rows;
-  a.m_log2 = false;
   a.out = out;
   a.out_dtype = out_dtype;
   a.out_m = out_m;

@@ -32,6 +32,9 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNW = 4;            // waves per workgroup = one partition
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 1
+#endif
 constexpr int kThreads = 64 * kNW;
 
 struct DecodeParams {
@@ -48,9 +51,10 @@ struct DecodeParams {
   const int32_t* seq_lens;
   float scale_log2;          // softmax scale * log2(e)
   int P, PB;
-  float* part_o;             // [B*hq][P][D], unnormalised, relative to part_m
-  float* part_m;             // [B*hq][P], log2 units
-  float* part_l;             // [B*hq][P]
+  int64_t rows;              // B * hq
+  float* part_o;             // [P][B*hq][D], unnormalised, relative to part_m
+  float* part_m;             // [P][B*hq], natural-log units
+  float* part_l;             // [P][B*hq]
 };
 
 __device__ __forceinline__ int seq_len_clamped(const DecodeParams& p, int b) {
@@ -67,24 +71,30 @@ struct SoftState {
 };
 
 // Online-softmax step over this lane's 4 scores x (log2 units, -inf = masked).
-// The max is taken over the 16 tokens of the page (the 4 lanes of one head).
+// The running max m is shared by the 4 lanes of a head and is only raised when
+// some score exceeds it by more than kLazy: weights then stay below 2^kLazy
+// (well inside fp16 / bf16 / fp32 range) and the result is the same, while the
+// cross-lane max and the rescale of O run only on the pages that raise m.
+constexpr float kLazy = 8.0f;
+
 template <int D>
 __device__ __forceinline__ void online_update(SoftState<D>& st, const float (&x)[4],
                                               float (&pw)[4]) {
-  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
-  st.l = st.l * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
-  if (__ballot(alpha != 1.0f) != 0ull) {
+  const float local = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (__ballot(local > st.m + kLazy) != 0ull) {
+    float mx = fmaxf(local, __shfl_xor(local, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) st.o[n] *= alpha;
+    st.m = m_new;
   }
-  st.m = m_new;
+  const float m_use = st.m == -INFINITY ? 0.f : st.m;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+  st.l += (pw[0] + pw[1]) + (pw[2] + pw[3]);
 }
 
 // Number of this lane's 4 tokens (starting at tok) that are below n, as a mask
@@ -101,15 +111,25 @@ struct BF16Page {
   u32x2 v[D / 16];     // V^T[16n + l%16][4*(l/16) .. +4]
 };
 
+// K/V pages are read once per step: streaming loads (non-temporal when
+// PKV_DECODE_NT is set).
+template <typename T>
+__device__ __forceinline__ T stream_load(const uint8_t* p) {
+#if PKV_DECODE_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+#else
+  return *reinterpret_cast<const T*>(p);
+#endif
+}
+
 template <int D>
 __device__ __forceinline__ void load_page(BF16Page<D>& pg, const uint8_t* kp, const uint8_t* vp,
                                           int col, int grp) {
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c)
-    pg.k[c] = *reinterpret_cast<const u32x4*>(kp + 2 * (col * D + 32 * c + 8 * grp));
+  for (int c = 0; c < D / 32; ++c) pg.k[c] = stream_load<u32x4>(kp + 2 * (col * D + 32 * c + 8 * grp));
 #pragma unroll
   for (int n = 0; n < D / 16; ++n)
-    pg.v[n] = *reinterpret_cast<const u32x2*>(vp + 2 * ((16 * n + col) * 16 + 4 * grp));
+    pg.v[n] = stream_load<u32x2>(vp + 2 * ((16 * n + col) * 16 + 4 * grp));
 }
 
 template <int D>
@@ -166,26 +186,29 @@ template <int D>
 __device__ __forceinline__ void load_page(FP8Page<D>& pg, const uint8_t* kp, const uint8_t* vp,
                                           int col, int grp) {
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c)
-    pg.k[c] = *reinterpret_cast<const u32x2*>(kp + col * D + 32 * c + 8 * grp);
+  for (int c = 0; c < D / 32; ++c) pg.k[c] = stream_load<u32x2>(kp + col * D + 32 * c + 8 * grp);
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n)
-    pg.v[n] = *reinterpret_cast<const uint32_t*>(vp + (16 * n + col) * 16 + 4 * grp);
+  for (int n = 0; n < D / 16; ++n) pg.v[n] = stream_load<uint32_t>(vp + (16 * n + col) * 16 + 4 * grp);
 }
 
+// E4M3 -> fp16 with the gfx950 scaled convert at scale 1: every finite E4M3
+// value (max 448, subnormals included) is exact in fp16.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(uint32_t codes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, HI));
+}
 __device__ __forceinline__ f16x8 codes8_to_f16(u32x2 c) {
-  u32x4 h = {e4m3x2_to_f16x2_scaled(c.x & 0xffffu), e4m3x2_to_f16x2_scaled(c.x >> 16),
-             e4m3x2_to_f16x2_scaled(c.y & 0xffffu), e4m3x2_to_f16x2_scaled(c.y >> 16)};
+  u32x4 h = {cvt2<false>(c.x), cvt2<true>(c.x), cvt2<false>(c.y), cvt2<true>(c.y)};
   return __builtin_bit_cast(f16x8, h);
 }
 __device__ __forceinline__ f16x4 codes4_to_f16(uint32_t c) {
-  u32x2 h = {e4m3x2_to_f16x2_scaled(c & 0xffffu), e4m3x2_to_f16x2_scaled(c >> 16)};
+  u32x2 h = {cvt2<false>(c), cvt2<true>(c)};
   return __builtin_bit_cast(f16x4, h);
 }
 
-// E4M3 values enter the MFMA as fp16 equal to value * 2^-8; the 2^8 and the
-// per-block scales are applied in fp32 to the scores and to each page's PV
-// product.
+// E4M3 values enter the MFMA as exact fp16; the per-block scales are applied
+// in fp32 to the scores and to each page's PV product.
 template <int D>
 __device__ __forceinline__ void compute_page(SoftState<D>& st, const FP8Page<D>& pg,
                                              const u32x4 (&qf)[D / 32], int tok, int n,
@@ -196,7 +219,7 @@ __device__ __forceinline__ void compute_page(SoftState<D>& st, const FP8Page<D>&
     s = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16(pg.k[c]),
                                               __builtin_bit_cast(f16x8, qf[c]), s, 0, 0, 0);
   const int vc = valid_count(tok, n);
-  const float kf = sl2 * 256.f * pg.ks;
+  const float kf = sl2 * pg.ks;
   float x[4], pw[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = i < vc ? s[i] * kf : -INFINITY;
@@ -205,14 +228,15 @@ __device__ __forceinline__ void compute_page(SoftState<D>& st, const FP8Page<D>&
 #pragma unroll
   for (int i = 0; i < 4; ++i) pb[i] = (_Float16)pw[i];
   const uint32_t keep = vc >= 4 ? 0xffffffffu : ((1u << (8 * vc)) - 1u);
-  const float vf = 256.f * pg.vs;
+  const float vf = pg.vs;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 t[D / 16];     // one product per tile, so the MFMAs issue back to back
 #pragma unroll
-  for (int nn = 0; nn < D / 16; ++nn) {
-    const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_f16(pg.v[nn] & keep), pb,
-                                                         zero, 0, 0, 0);
-    st.o[nn] += t * vf;
-  }
+  for (int nn = 0; nn < D / 16; ++nn)
+    t[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_f16(pg.v[nn] & keep), pb, zero, 0, 0,
+                                                 0);
+#pragma unroll
+  for (int nn = 0; nn < D / 16; ++nn) st.o[nn] += t[nn] * vf;
 }
 
 template <int D, int KVF>
@@ -228,17 +252,21 @@ __device__ __forceinline__ bool issue_page(PageT<D, KVF>& pg, const DecodeParams
   const uint8_t* vp = p.v + base + (int64_t)kvh * D * kBlock * esz;
   load_page<D>(pg, kp, vp, col, grp);
   if constexpr (KVF == PKV_FP8_E4M3) {
-    const int64_t si = (int64_t)(ok ? blk : 0) * p.hkv + kvh;
-    pg.ks = p.k_scale[si];
-    pg.vs = p.v_scale[si];
+    // vector loads (the address is forced into a VGPR), so the scales are
+    // ordered with the page loads instead of waiting on the scalar queue
+    const float* ks = p.k_scale + (int64_t)(ok ? blk : 0) * p.hkv + kvh;
+    const float* vs = p.v_scale + (int64_t)(ok ? blk : 0) * p.hkv + kvh;
+    asm volatile("" : "+v"(ks), "+v"(vs));
+    pg.ks = *ks;
+    pg.vs = *vs;
   }
   return ok;
 }
 
 // grid (P, hkv * HG, B): one workgroup per (partition, kv head, 16-head group,
-// sequence); wave w takes pages w, w+4, ... of the partition, two in flight.
+// sequence); wave w takes a contiguous quarter of the partition's pages.
 template <int D, int KVF>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 3) void decode_mfma_kernel(DecodeParams p) {
   __shared__ float sm_o[kNW][16][D];
   __shared__ float sm_m[kNW][16];
   __shared__ float sm_l[kNW][16];
@@ -288,31 +316,44 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
   for (int nn = 0; nn < D / 16; ++nn) st.o[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* trow = p.tables + (int64_t)b * p.maxb;
-  const int mine = j1 - j0 - w;
-  const int cnt = mine > 0 ? (mine + kNW - 1) / kNW : 0;
-  // table entries of this wave's pages, 64 at a time: lane i -> page k = base + i
-  auto table_chunk = [&](int base) {
-    const int jj = j0 + w + kNW * (base + lane);
-    return jj < j1 ? trow[jj] : -1;
-  };
-  int tabv = cnt > 0 ? table_chunk(0) : -1;
-  auto blk_of = [&](int k) {
-    if ((k & 63) == 0 && k > 0) tabv = table_chunk(k);
-    return __builtin_amdgcn_readlane(tabv, k & 63);
-  };
+  // this wave's pages: a contiguous quarter of the partition
+  const int per_w = (j1 - j0 + kNW - 1) / kNW;
+  const int pw0 = j0 + w * per_w;
+  const int cnt = max(0, min(per_w, j1 - pw0));
+  // table entries through the constant address space: wave-uniform scalar loads
+  typedef const __attribute__((address_space(4))) int32_t ctab_t;
+  ctab_t* trow = (ctab_t*)(p.tables + (int64_t)b * p.maxb);
 
-  PageT<D, KVF> pa, pb;
-  bool ok_a = false, ok_b = false;
-  if (cnt > 0) ok_a = issue_page<D, KVF>(pa, p, blk_of(0), kvh, col, grp);
-  for (int k = 0; k < cnt; k += 2) {
-    if (k + 1 < cnt) ok_b = issue_page<D, KVF>(pb, p, blk_of(k + 1), kvh, col, grp);
-    if (ok_a)
-      compute_page<D>(st, pa, qf, (j0 + w + kNW * k) * kBlock + 4 * grp, n, p.scale_log2);
-    if (k + 1 >= cnt) break;
-    if (k + 2 < cnt) ok_a = issue_page<D, KVF>(pa, p, blk_of(k + 2), kvh, col, grp);
-    if (ok_b)
-      compute_page<D>(st, pb, qf, (j0 + w + kNW * (k + 1)) * kBlock + 4 * grp, n, p.scale_log2);
+  // Two pages in flight: the next page's loads are always issued (clamped to
+  // the wave's last page) so the number of loads outstanding at each compute
+  // is fixed and only the page being computed is waited for.
+  // Two pages in flight per wave: page k+1's loads are issued before page k
+  // is computed.  Every path issues exactly the pages the wave owns (the tail
+  // is peeled), so the count of loads outstanding at each compute is fixed
+  // and only the page being computed is waited for.  Table entries are read
+  // one step ahead of the loads that need them.
+  if (cnt > 0) {
+    PageT<D, KVF> pa, pb;
+    const int last = cnt - 1;
+    bool ok_a = issue_page<D, KVF>(pa, p, trow[pw0], kvh, col, grp);
+    int tb1 = trow[pw0 + min(1, last)];
+    int tb2 = trow[pw0 + min(2, last)];
+    int k = 0;
+    for (; k + 2 <= last; k += 2) {
+      const bool ok_b = issue_page<D, KVF>(pb, p, tb1, kvh, col, grp);
+      if (ok_a) compute_page<D>(st, pa, qf, (pw0 + k) * kBlock + 4 * grp, n, p.scale_log2);
+      ok_a = issue_page<D, KVF>(pa, p, tb2, kvh, col, grp);
+      tb1 = trow[pw0 + min(k + 3, last)];
+      tb2 = trow[pw0 + min(k + 4, last)];
+      if (ok_b) compute_page<D>(st, pb, qf, (pw0 + k + 1) * kBlock + 4 * grp, n, p.scale_log2);
+    }
+    if (k + 1 <= last) {
+      const bool ok_b = issue_page<D, KVF>(pb, p, tb1, kvh, col, grp);
+      if (ok_a) compute_page<D>(st, pa, qf, (pw0 + k) * kBlock + 4 * grp, n, p.scale_log2);
+      if (ok_b) compute_page<D>(st, pb, qf, (pw0 + k + 1) * kBlock + 4 * grp, n, p.scale_log2);
+    } else if (ok_a) {
+      compute_page<D>(st, pa, qf, (pw0 + k) * kBlock + 4 * grp, n, p.scale_log2);
+    }
   }
 
   // wave state -> LDS (sum l over the 4 lanes of each head)
@@ -330,32 +371,35 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 
   // combine the 4 waves: thread -> (head g, D/16 dims)
   const int g = threadIdx.x >> 4, dc = threadIdx.x & 15;
-  if (hg * 16 + g >= p.G) return;
-  float M = -INFINITY;
-#pragma unroll
-  for (int ww = 0; ww < kNW; ++ww) M = fmaxf(M, sm_m[ww][g]);
-  float a[kNW];
-  float L = 0.f;
-#pragma unroll
-  for (int ww = 0; ww < kNW; ++ww) {
-    const float mw = sm_m[ww][g];
-    a[ww] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-    L += a[ww] * sm_l[ww][g];
-  }
+  const bool g_ok = hg * 16 + g < p.G;
+  if (!g_ok) return;
   const int64_t row = (int64_t)b * p.hq + (int64_t)kvh * p.G + hg * 16 + g;
-  float* po = p.part_o + (row * p.P + part) * D;
   constexpr int DPT = D / 16;
+  {
+    float M = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < DPT; ++e) {
-    const int d = dc * DPT + e;
-    float acc = 0.f;
+    for (int ww = 0; ww < kNW; ++ww) M = fmaxf(M, sm_m[ww][g]);
+    float a[kNW];
+    float L = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kNW; ++ww) acc += a[ww] * sm_o[ww][g][d];
-    po[d] = acc;
-  }
-  if (dc == 0) {
-    p.part_m[row * p.P + part] = M;
-    p.part_l[row * p.P + part] = L;
+    for (int ww = 0; ww < kNW; ++ww) {
+      const float mw = sm_m[ww][g];
+      a[ww] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += a[ww] * sm_l[ww][g];
+    }
+    float* po = p.part_o + ((int64_t)part * p.rows + row) * D;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      const int d = dc * DPT + e;
+      float acc = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kNW; ++ww) acc += a[ww] * sm_o[ww][g][d];
+      po[d] = acc;
+    }
+    if (dc == 0) {
+      p.part_m[(int64_t)part * p.rows + row] = M == -INFINITY ? -INFINITY : M * kLn2;
+      p.part_l[(int64_t)part * p.rows + row] = L;
+    }
   }
 }
 
@@ -429,11 +473,11 @@ __global__ __launch_bounds__(64) void decode_simple_kernel(DecodeParams p, int D
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int d = lane + 64 * e;
-      if (d < D) p.part_o[(row * p.P + part) * D + d] = o[e];
+      if (d < D) p.part_o[((int64_t)part * p.rows + row) * D + d] = o[e];
     }
     if (lane == 0) {
-      p.part_m[row * p.P + part] = m;
-      p.part_l[row * p.P + part] = l;
+      p.part_m[(int64_t)part * p.rows + row] = m == -INFINITY ? -INFINITY : m * kLn2;
+      p.part_l[(int64_t)part * p.rows + row] = l;
     }
   }
 }
@@ -460,28 +504,20 @@ DecodePlan plan_decode(int B, int hq, int hkv, int head_dim, int maxb, int parti
   plan.partition_blocks = pb;
   plan.partitions = (maxb + pb - 1) / pb;
   if (plan.partitions < 1) plan.partitions = 1;
+  // Workspace: [O~][m][l], each 256-byte aligned.
   const size_t rows = (size_t)B * hq * plan.partitions;
-  size_t bytes = rows * head_dim * sizeof(float);
-  bytes = (bytes + 255) & ~size_t(255);
+  size_t bytes = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
   bytes += 2 * ((rows * sizeof(float) + 255) & ~size_t(255));
   plan.ws_bytes = bytes;
   return plan;
 }
 
-hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, int hq,
-                         const int32_t* tables, int maxb, const int32_t* seq_lens, float scale,
-                         const DecodePlan& plan, void* out, float* out_lse, void* ws,
-                         hipStream_t s) {
+hipError_t launch_decode_partial(const CacheView& c, const void* q, int q_dtype, int B, int hq,
+                                 const int32_t* tables, int maxb, const int32_t* seq_lens,
+                                 float scale, const DecodePlan& plan, float* part_o,
+                                 float* part_m, float* part_l, hipStream_t s) {
   if (B == 0) return hipSuccess;
   const int D = c.head_dim;
-  const size_t rows = (size_t)B * hq * plan.partitions;
-  uint8_t* w = static_cast<uint8_t*>(ws);
-  float* part_o = reinterpret_cast<float*>(w);
-  size_t off = (rows * D * sizeof(float) + 255) & ~size_t(255);
-  float* part_m = reinterpret_cast<float*>(w + off);
-  off += (rows * sizeof(float) + 255) & ~size_t(255);
-  float* part_l = reinterpret_cast<float*>(w + off);
-
   const int esz = c.kv_dtype == PKV_F32 ? 4 : (c.kv_dtype == PKV_BF16 ? 2 : 1);
   DecodeParams p{};
   p.k = static_cast<const uint8_t*>(c.k);
@@ -502,6 +538,7 @@ hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, 
   p.scale_log2 = scale * kLog2e;
   p.P = plan.partitions;
   p.PB = plan.partition_blocks;
+  p.rows = (int64_t)B * hq;
   p.part_o = part_o;
   p.part_m = part_m;
   p.part_l = part_l;
@@ -526,27 +563,50 @@ hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, 
       else return hipErrorInvalidValue;
     }
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
 
+hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, int hq,
+                         const int32_t* tables, int maxb, const int32_t* seq_lens, float scale,
+                         const DecodePlan& plan, void* out, float* out_lse, void* ws,
+                         hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const int D = c.head_dim;
+  const size_t rows = (size_t)B * hq * plan.partitions;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  float* part_o = reinterpret_cast<float*>(w);
+  size_t off = (rows * D * sizeof(float) + 255) & ~size_t(255);
+  float* part_m = reinterpret_cast<float*>(w + off);
+  off += (rows * sizeof(float) + 255) & ~size_t(255);
+  float* part_l = reinterpret_cast<float*>(w + off);
+  hipError_t e = launch_decode_partial(c, q, q_dtype, B, hq, tables, maxb, seq_lens, scale, plan,
+                                       part_o, part_m, part_l, s);
+  if (e != hipSuccess) return e;
+  return launch_merge(partition_merge_args(plan.partitions, (int64_t)B * hq, D, part_o, part_m,
+                                           part_l, out, q_dtype, out_lse),
+                      s);
+}
+
+MergeArgs partition_merge_args(int S, int64_t rows, int D, const float* part_o,
+                               const float* part_m, const float* part_l, void* out,
+                               int out_dtype, float* out_lse) {
   MergeArgs a{};
-  a.S = plan.partitions;
-  a.rows = (int64_t)B * hq;
+  a.S = S;
+  a.rows = rows;
   a.D = D;
   a.o = part_o;
-  a.o_row = (int64_t)plan.partitions * D;
-  a.o_part = D;
+  a.o_row = D;
+  a.o_part = rows * D;
   a.m = part_m;
   a.l = part_l;
-  a.ml_row = plan.partitions;
-  a.ml_part = 1;
-  a.m_log2 = true;
+  a.ml_row = 1;
+  a.ml_part = rows;
   a.out = out;
-  a.out_dtype = q_dtype;
+  a.out_dtype = out_dtype;
   a.out_m = nullptr;
   a.out_l = nullptr;
   a.out_lse = out_lse;
-  return launch_merge(a, s);
+  return a;
 }
 
 }  // namespace pkv

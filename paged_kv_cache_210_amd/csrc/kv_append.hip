@@ -31,8 +31,98 @@ __device__ __forceinline__ T load_elem(const void* p, int64_t i) {
   return reinterpret_cast<const T*>(p)[i];
 }
 
-// One wave per token, four tokens per 256-thread workgroup.  Same-type caches
-// copy raw bits; E4M3 caches quantise f32(x) * f32(1/scale) of the block.
+// One wave per token, four tokens per 256-thread workgroup.  Lane chunks are
+// 8 consecutive elements of the token's [Hkv][d] row; each lane issues all of
+// its loads before any store, so a small append (one token per sequence in a
+// decode step) costs about one memory round trip.  K rows are contiguous in a
+// page (one 8-element store per chunk); V elements of one token are 16 apart.
+// Same-type caches copy raw bits; E4M3 caches quantise f32(x) * f32(1/scale)
+// with the scale of the destination (block, head).
+constexpr int kChunk = 8;      // elements per lane chunk
+constexpr int kUnroll = 4;     // chunks in flight per lane
+
+template <int SRC>
+struct SrcChunk;
+template <>
+struct SrcChunk<PKV_BF16> {
+  u32x4 k, v;                  // 8 bf16
+};
+template <>
+struct SrcChunk<PKV_F32> {
+  u32x4 k[2], v[2];            // 8 fp32
+};
+
+template <int SRC>
+__device__ __forceinline__ void load_chunk(SrcChunk<SRC>& c, const void* k, const void* v,
+                                           int64_t e) {
+  if constexpr (SRC == PKV_BF16) {
+    c.k = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(k) + e);
+    c.v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(v) + e);
+  } else {
+    c.k[0] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(k) + e);
+    c.k[1] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(k) + e + 4);
+    c.v[0] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(v) + e);
+    c.v[1] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(v) + e + 4);
+  }
+}
+
+// element i (0..7) of a chunk as fp32
+template <int SRC>
+__device__ __forceinline__ float chunk_f32(const u32x4& x0, const u32x4* x, int i) {
+  if constexpr (SRC == PKV_BF16) {
+    const uint32_t w = x0[i >> 1];
+    return bf16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
+  } else {
+    return __uint_as_float(x[i >> 2][i & 3]);
+  }
+}
+
+template <int SRC, int DST>
+__device__ __forceinline__ void store_chunk(const AppendParams& p, const SrcChunk<SRC>& c,
+                                            int blk, int64_t base, int off, int e) {
+  const int h = e / p.D;
+  const int d = e - h * p.D;                 // chunk never crosses a head (D % 8 == 0)
+  const int64_t kd = base + (int64_t)h * kBlock * p.D + (int64_t)off * p.D + d;
+  const int64_t vd = base + (int64_t)h * p.D * kBlock + (int64_t)d * kBlock + off;
+  if constexpr (DST == PKV_FP8_E4M3) {
+    const int64_t si = (int64_t)blk * p.hkv + h;
+    const float inv_k = __frcp_rn(p.k_scale[si]);
+    const float inv_v = __frcp_rn(p.v_scale[si]);
+    const u32x4* kx = nullptr;
+    const u32x4* vx = nullptr;
+    u32x4 k0{}, v0{};
+    if constexpr (SRC == PKV_BF16) {
+      k0 = c.k;
+      v0 = c.v;
+    } else {
+      kx = c.k;
+      vx = c.v;
+    }
+    u32x2 codes = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const uint32_t ck = e4m3_encode(__fmul_rn(chunk_f32<SRC>(k0, kx, i), inv_k));
+      codes[i >> 2] |= ck << (8 * (i & 3));
+      const uint32_t cv = e4m3_encode(__fmul_rn(chunk_f32<SRC>(v0, vx, i), inv_v));
+      p.v_pool[vd + (int64_t)i * kBlock] = (uint8_t)cv;
+    }
+    *reinterpret_cast<u32x2*>(p.k_pool + kd) = codes;
+  } else if constexpr (DST == PKV_BF16) {
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.k_pool) + kd) = c.k;
+    uint16_t* vp = reinterpret_cast<uint16_t*>(p.v_pool) + vd;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      vp[(int64_t)i * kBlock] = (uint16_t)((i & 1) ? (c.v[i >> 1] >> 16) : (c.v[i >> 1] & 0xffffu));
+  } else {
+    float* kp = reinterpret_cast<float*>(p.k_pool) + kd;
+    *reinterpret_cast<u32x4*>(kp) = c.k[0];
+    *reinterpret_cast<u32x4*>(kp + 4) = c.k[1];
+    float* vp = reinterpret_cast<float*>(p.v_pool) + vd;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) vp[(int64_t)i * kBlock] = __uint_as_float(c.v[i >> 2][i & 3]);
+  }
+}
+
 template <int SRC, int DST>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -45,32 +135,20 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   if (blk < 0 || blk >= p.num_blocks) return;
   const int off = pos & (kBlock - 1);
   const int HD = p.hkv * p.D;
+  const int nch = HD / kChunk;
   const int64_t src0 = (int64_t)tok * HD;
   const int64_t base = (int64_t)blk * p.block_stride;
-  for (int e = lane; e < HD; e += 64) {
-    const int h = e / p.D;
-    const int d = e - h * p.D;
-    const int64_t kd = base + (int64_t)h * kBlock * p.D + (int64_t)off * p.D + d;
-    const int64_t vd = base + (int64_t)h * p.D * kBlock + (int64_t)d * kBlock + off;
-    if constexpr (DST == PKV_FP8_E4M3) {
-      float xk, xv;
-      if constexpr (SRC == PKV_BF16) {
-        xk = bf16_bits_to_f32(load_elem<uint16_t>(p.k_new, src0 + e));
-        xv = bf16_bits_to_f32(load_elem<uint16_t>(p.v_new, src0 + e));
-      } else {
-        xk = load_elem<float>(p.k_new, src0 + e);
-        xv = load_elem<float>(p.v_new, src0 + e);
-      }
-      const float inv_k = __frcp_rn(p.k_scale[(int64_t)blk * p.hkv + h]);
-      const float inv_v = __frcp_rn(p.v_scale[(int64_t)blk * p.hkv + h]);
-      p.k_pool[kd] = (uint8_t)e4m3_encode(__fmul_rn(xk, inv_k));
-      p.v_pool[vd] = (uint8_t)e4m3_encode(__fmul_rn(xv, inv_v));
-    } else if constexpr (DST == PKV_BF16) {
-      reinterpret_cast<uint16_t*>(p.k_pool)[kd] = load_elem<uint16_t>(p.k_new, src0 + e);
-      reinterpret_cast<uint16_t*>(p.v_pool)[vd] = load_elem<uint16_t>(p.v_new, src0 + e);
-    } else {
-      reinterpret_cast<float*>(p.k_pool)[kd] = load_elem<float>(p.k_new, src0 + e);
-      reinterpret_cast<float*>(p.v_pool)[vd] = load_elem<float>(p.v_new, src0 + e);
+  for (int c0 = 0; c0 < nch; c0 += 64 * kUnroll) {
+    SrcChunk<SRC> ch[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < nch) load_chunk<SRC>(ch[u], p.k_new, p.v_new, src0 + (int64_t)c * kChunk);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < nch) store_chunk<SRC, DST>(p, ch[u], blk, base, off, c * kChunk);
     }
   }
 }

@@ -56,16 +56,6 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | code;
 }
 
-// E4M3 byte -> fp16 bit pattern whose value is the E4M3 value times 2^-8.
-// Exact for every finite code, subnormals included (fp16 has one more
-// exponent bit and the bias differs by 8).
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2_scaled(uint32_t two_bytes) {
-  // two_bytes: byte0 in bits 0..7, byte1 in bits 8..15 -> fp16 in halves 0, 1
-  const uint32_t lo = ((two_bytes & 0x7fu) << 7) | ((two_bytes & 0x80u) << 8);
-  const uint32_t hi = ((two_bytes & 0x7f00u) << 15) | ((two_bytes & 0x8000u) << 16);
-  return lo | hi;
-}
-
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
@@ -109,6 +99,10 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int B, int hq, int hkv, int head_dim, int maxb, int partition_blocks,
                        int q_dtype, int kv_dtype);
+hipError_t launch_decode_partial(const CacheView& c, const void* q, int q_dtype, int B, int hq,
+                                 const int32_t* tables, int maxb, const int32_t* seq_lens,
+                                 float scale, const DecodePlan& plan, float* part_o,
+                                 float* part_m, float* part_l, hipStream_t s);
 hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, int hq,
                          const int32_t* tables, int maxb, const int32_t* seq_lens, float scale,
                          const DecodePlan& plan, void* out, float* out_lse, void* ws,
@@ -126,10 +120,9 @@ struct MergeArgs {
   int D;
   const float* o;      // O~ of part s, row r at o + r*o_row + s*o_part
   int64_t o_row, o_part;
-  const float* m;      // m of part s, row r at m + r*ml_row + s*ml_part
+  const float* m;      // m (natural units) of part s, row r at m + r*ml_row + s*ml_part
   const float* l;
   int64_t ml_row, ml_part;
-  bool m_log2;         // m stored in log2 units (internal decode partials)
   void* out;
   int out_dtype;
   float* out_m;
@@ -137,5 +130,9 @@ struct MergeArgs {
   float* out_lse;
 };
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+// Merge arguments for partials laid out part-major: O~ [S][rows][D], m/l [S][rows].
+MergeArgs partition_merge_args(int S, int64_t rows, int D, const float* part_o,
+                               const float* part_m, const float* part_l, void* out,
+                               int out_dtype, float* out_lse);
 
 }  // namespace pkv

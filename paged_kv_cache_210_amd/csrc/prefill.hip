@@ -36,6 +36,7 @@ constexpr int ROWS_W = 32;               // query rows per wave
 constexpr int NWAVE = 4;
 constexpr int BM = ROWS_W * NWAVE;       // query rows per workgroup
 constexpr int TILE_BYTES = BN * D * 2;   // 16 KiB for K, same for V
+constexpr float kLazy = 8.0f;            // log2 headroom of the running max
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -143,6 +144,105 @@ __device__ __forceinline__ void store_tile(uint8_t* ks, uint8_t* vs, const TileR
   }
 }
 
+// One 64-token K/V tile for this wave's 32 query rows: S^T = K Q^T, online
+// softmax, O^T += V^T P^T.  The per-score visibility test runs only on tiles
+// that cross kv_begin / kv_end or the causal diagonal of this wave's rows
+// (need_mask, uniform over the wave).
+struct RowState {
+  f32x16 o[4];
+  float m, l, mtrue;
+};
+
+template <bool NEG_SCALE>
+__device__ __forceinline__ void attend_tile(RowState& st, const uint8_t* ks, const uint8_t* vs,
+                                            const u32x4 (&qf)[8], const PrefillParams& p, int tb,
+                                            int my_pos, int qr, int hi, bool need_mask) {
+  // ---- S^T = K Q^T over two 32-token halves of the tile
+  f32x16 s[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+    const int t = 32 * mt + qr;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + k_lds_off(t, 2 * c + hi));
+      s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                     __builtin_bit_cast(bf16x8, qf[c]), s[mt], 0,
+                                                     0, 0);
+    }
+  }
+  // ---- mask, online softmax in log2 units.  The largest scaled score is
+  // c * max(s) for c > 0 and c * min(s) for c < 0, so the scale is folded
+  // into one FMA per score: p = exp2(s * c - m).
+  const float c = p.scale_log2;
+  const float hidden = NEG_SCALE ? INFINITY : -INFINITY;   // s * c == -inf
+  if (need_mask) {
+    // visible keys of this lane's row: [lo, hi_) relative to the tile
+    const int lo = p.kv_begin - tb - 4 * hi;
+    const int hi_ = (p.causal ? min(p.kv_end, my_pos + 1) : p.kv_end) - tb - 4 * hi;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ti = 32 * mt + 8 * (r >> 2) + (r & 3);
+        s[mt][r] = (ti >= lo && ti < hi_) ? s[mt][r] : hidden;
+      }
+  }
+  float ext = hidden;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ext = NEG_SCALE ? fminf(ext, s[mt][r]) : fmaxf(ext, s[mt][r]);
+  // The running max is raised only when a score exceeds it by more than
+  // kLazy (weights stay below 2^kLazy); the row's lane pair then agrees on the
+  // new max and O, l are rescaled.  Same result, and the common tile needs no
+  // cross-lane step and no rescale.
+  const float lmx = ext == hidden ? -INFINITY : ext * c;
+  st.mtrue = fmaxf(st.mtrue, lmx);
+  if (__ballot(lmx > st.m + kLazy) != 0ull) {
+    const float pe = __shfl_xor(ext, 32);
+    const float e2 = NEG_SCALE ? fminf(ext, pe) : fmaxf(ext, pe);
+    const float mx = e2 == hidden ? -INFINITY : e2 * c;
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = st.m == -INFINITY ? 0.f : st.m;
+  // ---- O^T += V^T P^T, four 16-token k-steps, in fp16 (V was converted
+  // exactly when staged; fp16 weights carry 11 significant bits).  The row sum
+  // is taken over the rounded weights that enter the product, so the result
+  // stays an exact weighted average of V rows.
+  float rs = 0.f;
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      f16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pb[e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][8 * rr + e], c, -m_use));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 pr = {pb[2 * e], pb[2 * e + 1]};
+        rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
+      }
+      const int page = 2 * mt + rr;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int d = 32 * dt + qr;
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + v_lds_off(page, d, hi));
+        st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf), pb,
+                                                         st.o[dt], 0, 0, 0);
+      }
+    }
+  st.l += rs;
+}
+
 template <bool NEG_SCALE>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][2 * TILE_BYTES];
@@ -187,12 +287,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const int w_maxpos = p.q_pos0 + w_last;
   const bool wave_live = wrow0 < p.T;
 
-  f32x16 o[4];
+  RowState st;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
+    for (int r = 0; r < 16; ++r) st.o[dt][r] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.mtrue = -INFINITY;           // this lane's exact max of the scaled scores
 
   TileRegs regs;
   bool valid = false;
@@ -213,81 +315,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     if (wave_sees) {
       const uint8_t* ks = smem[buf];
       const uint8_t* vs = smem[buf] + TILE_BYTES;
-      // ---- S^T = K Q^T over two 32-token halves of the tile
-      f32x16 s[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-        const int t = 32 * mt + qr;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + k_lds_off(t, 2 * c + hi));
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                         __builtin_bit_cast(bf16x8, qf[c]),
-                                                         s[mt], 0, 0, 0);
-        }
-      }
-      // ---- mask, online softmax in log2 units.  The largest scaled score
-      // is c * max(s) for c > 0 and c * min(s) for c < 0, so the scale is
-      // folded into one FMA per score: p = exp2(s * c - m).
       const bool need_mask = tb < p.kv_begin || tb + BN > p.kv_end ||
                              (p.causal && tb + BN - 1 > w_minpos);
-      const float c = p.scale_log2;
-      const float hidden = NEG_SCALE ? INFINITY : -INFINITY;   // s * c == -inf
-      float ext = hidden;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[mt][r];
-          if (need_mask) {
-            const int ta = tb + 32 * mt + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool vis = ta >= p.kv_begin && ta < p.kv_end && (!p.causal || ta <= my_pos);
-            x = vis ? x : hidden;
-          }
-          s[mt][r] = x;
-          ext = NEG_SCALE ? fminf(ext, x) : fmaxf(ext, x);
-        }
-      ext = NEG_SCALE ? fminf(ext, __shfl_xor(ext, 32)) : fmaxf(ext, __shfl_xor(ext, 32));
-      const float mx = ext == hidden ? -INFINITY : ext * c;
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      m = m_new;
-      if (__ballot(alpha != 1.0f) != 0ull) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-      }
-      // ---- O^T += V^T P^T, four 16-token k-steps, in fp16 (V was converted
-      // exactly when staged; fp16 weights carry 11 significant bits).  The
-      // row sum is taken over the rounded weights that enter the product, so
-      // the result stays an exact weighted average of V rows.
-      float rs = 0.f;
-      const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          f16x8 pb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pb[e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][8 * rr + e], c, -m_use));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const f16x2 pr = {pb[2 * e], pb[2 * e + 1]};
-            rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
-          }
-          const int page = 2 * mt + rr;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const int d = 32 * dt + qr;
-            const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + v_lds_off(page, d, hi));
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf), pb,
-                                                          o[dt], 0, 0, 0);
-          }
-        }
-      l = l * alpha + rs;
+      attend_tile<NEG_SCALE>(st, ks, vs, qf, p, tb, my_pos, qr, hi, need_mask);
     }
 
     if (more) {
@@ -300,7 +330,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   }
 
   // ---- epilogue: row sum over the lane pair, then normalise or emit partials
-  l += __shfl_xor(l, 32);
+  float l = st.l + __shfl_xor(st.l, 32);
+  const float mtrue = fmaxf(st.mtrue, __shfl_xor(st.mtrue, 32));
+  float m = st.m;
+  f32x16 (&o)[4] = st.o;
   if (!row_ok) return;
   const bool empty = !(l > 0.f);
   const int64_t ro = (int64_t)my_row * p.hq + h;
@@ -321,6 +354,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       }
     if (p.out_lse && hi == 0) p.out_lse[ro] = empty ? -INFINITY : m * kLn2 + logf(l);
   } else {
+    // partials are exported relative to the exact row max (m <= mtrue <= m + kLazy)
+    const float f = empty ? 0.f : __builtin_amdgcn_exp2f(m - mtrue);
+    l *= f;
+    m = mtrue;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= f;
     float* op = p.part_o + ro * D;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)

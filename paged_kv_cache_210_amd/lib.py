@@ -65,6 +65,11 @@ _SIGS = {
     "pkv_paged_attn_decode": (c_int32, [POINTER(CacheDesc), c_void_p, c_int32, c_int32, c_int32,
                                         c_void_p, c_int32, c_void_p, c_float, c_int32, c_void_p,
                                         c_void_p, c_void_p, c_size_t, c_void_p]),
+    "pkv_decode_partitions": (c_int32, [POINTER(CacheDesc), c_int32, c_int32, c_int32, c_int32,
+                                        c_int32, POINTER(c_int32)]),
+    "pkv_paged_attn_decode_partial": (c_int32, [POINTER(CacheDesc), c_void_p, c_int32, c_int32,
+                                                c_int32, c_void_p, c_int32, c_void_p, c_float,
+                                                c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "pkv_paged_attn_prefill": (c_int32, [POINTER(CacheDesc), c_void_p, c_int32, c_int32, c_int32,
                                          c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                          c_float, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -296,6 +301,44 @@ def paged_attn_decode(cache: PagedCache, q, block_tables, seq_lens, scale=0.0,
     return out, out_lse
 
 
+def decode_partitions(cache, q_dtype, B, hq, max_blocks, partition_blocks=0):
+    out = c_int32()
+    d = cache.desc()
+    code = _DTYPE_CODE[q_dtype] if isinstance(q_dtype, torch.dtype) else q_dtype
+    _check(load().pkv_decode_partitions(ctypes.byref(d), code, B, hq, max_blocks,
+                                        partition_blocks, ctypes.byref(out)), "decode_partitions")
+    return out.value
+
+
+def paged_attn_decode_partial(cache: PagedCache, q, block_tables, seq_lens, scale=0.0,
+                              partition_blocks=0, part=None):
+    """Partial form: returns (part_o [P,B,Hq,d], part_m [P,B,Hq], part_l [P,B,Hq])."""
+    dev = cache.device
+    B, hq, D = q.shape
+    _need(q, None, "q", dev)
+    qc = _DTYPE_CODE.get(q.dtype)
+    if qc is None:
+        raise TypeError("q must be float32 or bfloat16")
+    _need(block_tables, torch.int32, "block_tables", dev)
+    _need(seq_lens, torch.int32, "seq_lens", dev, (B,))
+    P = decode_partitions(cache, q.dtype, B, hq, block_tables.shape[1], partition_blocks)
+    if part is None:
+        part = (torch.empty(P, B, hq, D, dtype=torch.float32, device=dev),
+                torch.empty(P, B, hq, dtype=torch.float32, device=dev),
+                torch.empty(P, B, hq, dtype=torch.float32, device=dev))
+    po, pm, pl = part
+    _need(po, torch.float32, "part_o", dev, (P, B, hq, D))
+    _need(pm, torch.float32, "part_m", dev, (P, B, hq))
+    _need(pl, torch.float32, "part_l", dev, (P, B, hq))
+    d = cache.desc()
+    _check(load().pkv_paged_attn_decode_partial(ctypes.byref(d), _p(q), qc, B, hq,
+                                                _p(block_tables), block_tables.shape[1],
+                                                _p(seq_lens), float(scale), int(partition_blocks),
+                                                _p(po), _p(pm), _p(pl), _stream(dev)),
+           "paged_attn_decode_partial")
+    return part
+
+
 def paged_attn_prefill(cache: PagedCache, q, q_pos0, block_table, kv_begin, kv_end, causal=True,
                        scale=0.0, partial=False, out=None, out_lse=None, part=None):
     dev = cache.device
@@ -323,7 +366,8 @@ def paged_attn_prefill(cache: PagedCache, q, q_pos0, block_table, kv_begin, kv_e
     return part if partial else (out, out_lse)
 
 
-def attn_lse_merge(part_o, part_m, part_l, out_dtype=torch.bfloat16, out=None, with_state=True):
+def attn_lse_merge(part_o, part_m, part_l, out_dtype=torch.bfloat16, out=None, with_state=True,
+                   out_lse=None):
     """part_o [S, rows..., d] fp32, part_m/part_l [S, rows...]; returns
     (O [rows..., d], M, L, lse)."""
     dev = part_o.device
@@ -336,11 +380,12 @@ def attn_lse_merge(part_o, part_m, part_l, out_dtype=torch.bfloat16, out=None, w
     _need(part_l, torch.float32, "part_l", dev, (S,) + rows_shape)
     if out is None:
         out = torch.empty(rows_shape + (D,), dtype=out_dtype, device=dev)
-    m = l = lse = None
+    m = l = None
+    lse = out_lse
     if with_state:
         m = torch.empty(rows_shape, dtype=torch.float32, device=dev)
         l = torch.empty_like(m)
-        lse = torch.empty_like(m)
+        lse = torch.empty_like(m) if lse is None else lse
     _check(load().pkv_attn_lse_merge(S, rows, D, _p(part_o), _p(part_m), _p(part_l), _p(out),
                                      _DTYPE_CODE[out.dtype], _p(m), _p(l), _p(lse), _stream(dev)),
            "attn_lse_merge")

@@ -257,3 +257,55 @@ def test_validate_tables_flags_bad_entries(lib):
     assert lib.validate_tables(t2, lens, 5) == 4                   # block 1 aliased
     lens2 = torch.tensor([40, 40], dtype=torch.int32, device=DEV)
     assert lib.validate_tables(t, lens2, 5) == 2                   # -1 covered by a length
+
+
+def test_decode_workspace_reused_across_calls(lib):
+    """One workspace serves consecutive calls of different shapes and
+    partition counts."""
+    cfg_a = synth.decode_config("ws-a", (300, 77, 1000), 32, 8, 128, seed_index=30)
+    cfg_b = synth.decode_config("ws-b", (2000,), 64, 8, 128, seed_index=31)
+    sa = _setup(lib, cfg_a)
+    sb = _setup(lib, cfg_b)
+    n = max(lib.decode_workspace_bytes(sa[4], torch.bfloat16, 3, 32, sa[3].shape[1], pb)
+            for pb in (4, 16)) + lib.decode_workspace_bytes(sb[4], torch.bfloat16, 1, 64,
+                                                            sb[3].shape[1], 8)
+    ws = torch.full((n + 256,), 0x7F, dtype=torch.uint8, device=DEV)   # stale contents
+    for rep in range(2):
+        for (inp, tables, dev, tdev, cache, lens), cfg, pb in ((sa, cfg_a, 4), (sb, cfg_b, 8),
+                                                              (sa, cfg_a, 16)):
+            out, lse = lib.paged_attn_decode(cache, dev["q"], tdev, lens, partition_blocks=pb,
+                                             ws=ws)
+            torch.cuda.synchronize()
+            _, ref = _oracle_decode(cfg, inp, tables)
+            compare_rows(out.float().cpu().numpy(), ref["o"], "bf16", f"{cfg.name} pb{pb} r{rep}")
+
+
+@pytest.mark.parametrize("pb", [0, 5])
+def test_decode_partial_form_matches_oracle_and_merges_to_decode(lib, pb):
+    cfg = synth.decode_config("partial", (100, 1, 333, 0), 16, 4, 128, seed_index=32)
+    inp, tables, dev, tdev, cache, lens = _setup(lib, cfg)
+    po, pm, pl = lib.paged_attn_decode_partial(cache, dev["q"], tdev, lens, partition_blocks=pb)
+    out, _, _, lse = lib.attn_lse_merge(po, pm, pl, out_dtype=torch.bfloat16)
+    ref_out, ref_lse = lib.paged_attn_decode(cache, dev["q"], tdev, lens, partition_blocks=pb)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    # each partition's state against the oracle over that partition's keys
+    P = po.shape[0]
+    PB = -(-tables.shape[1] // P)
+    oc = oracle_cache(cfg, inp, tables)
+    qn, qf = q_elements(inp["q"])
+    for b, n in enumerate(cfg.seq_lens):
+        for p_ in range(P):
+            a_, z_ = p_ * PB * 16, min((p_ + 1) * PB * 16, n)
+            if a_ >= z_:
+                assert np.all(pm[p_, b].cpu().numpy() == -np.inf)
+                assert np.all(pl[p_, b].cpu().numpy() == 0)
+                continue
+            r = O.prefill(oc, qn[b:b + 1], qf, n - 1, tables[b], a_, z_, True)
+            got_m = pm[p_, b].cpu().double().numpy()
+            got_l = pl[p_, b].cpu().double().numpy()
+            got_o = po[p_, b].cpu().double().numpy()
+            # states are defined up to the max shift: compare O~/l and m + ln l
+            np.testing.assert_allclose(got_m + np.log(got_l), r["lse"][0], atol=2e-3)
+            compare_rows(got_o / got_l[:, None], r["o"][0], "bf16", f"part {p_} seq {b}",
+                         out_fmt="f32")
