@@ -1,4 +1,4 @@
-// Chunked causal prefill against the paged KV cache, on bf16 MFMA.
+// Chunked causal prefill against the paged KV cache, on MFMA.
 //
 // What is computed: [P2] "Unlocking long context ..." section 4.1 (exact
 // attention, softmax(q K^T / sqrt(d)) V, with the causal flag of its flash
@@ -14,17 +14,22 @@
 // both products run on 32x32x16 MFMA:
 //   S^T[t][r]  = K[t][:] . Q[r][:]      bf16; A = K tile (LDS), B = Q (registers)
 //   O^T[d][r] += V^T[d][t] P^T[t][r]    fp16; A = V tile (LDS), B = P (registers)
-// V is converted to fp16 as it is staged (exact for bf16 values within fp16's
-// range) so the softmax weights can enter the second product with 11
-// significant bits instead of bf16's 8.
 // Computing S transposed puts one query row in each lane (plus its partner
-// lane l^32), so row max / sum need a single cross-lane step and the softmax
-// weights are already laid out as the B operand of the second product.
+// lane l^32), so a row's max and sum need at most one cross-lane step and the
+// softmax weights are already laid out as the B operand of the second
+// product.  V is converted to fp16 as it is staged (exact for bf16 values
+// within fp16's range) so the weights enter P V with 11 significant bits
+// instead of bf16's 8.
 //
-// Workgroup = 4 waves x 32 query rows of one head; K/V tiles of 64 tokens (4
-// pages) are gathered through the block table into double-buffered LDS.
+// Workgroup = 8 waves = the NH query heads of one kv head that share K/V x NR
+// blocks of 32 query rows (NH * NR = 8).  A 64-token K/V tile (4 pages) is
+// gathered through the block table once per workgroup into a three-deep LDS
+// ring, so one barrier per tile suffices.  Each wave software-pipelines: the
+// K Q^T products of tile j+1 are issued among the softmax instructions of tile
+// j, so the matrix cores and the vector ALUs work at the same time.
 // Workgroup i serves kv head i % Hkv, so with 8 kv heads every XCD streams one
-// head's K/V through its own L2.
+// head's K/V through its own L2; heavier (later) row blocks are dispatched
+// first.
 #include "pkv_common.h"
 
 namespace pkv {
@@ -33,9 +38,12 @@ namespace {
 constexpr int D = 128;
 constexpr int BN = 64;                   // tokens per K/V tile (4 pages)
 constexpr int ROWS_W = 32;               // query rows per wave
-constexpr int NWAVE = 4;
-constexpr int BM = ROWS_W * NWAVE;       // query rows per workgroup
+constexpr int NWAVE = 8;
+constexpr int NTHREADS = 64 * NWAVE;
 constexpr int TILE_BYTES = BN * D * 2;   // 16 KiB for K, same for V
+constexpr int BUF_BYTES = 2 * TILE_BYTES;
+constexpr int NBUF = 3;                  // LDS ring of K/V tiles
+constexpr int LDS_BYTES = NBUF * BUF_BYTES;
 constexpr float kLazy = 8.0f;            // log2 headroom of the running max
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -45,6 +53,7 @@ struct PrefillParams {
   const uint8_t* v;
   int64_t block_stride_bytes;
   int num_blocks, hkv, hq, G;
+  int NH, NR, HGR;                       // heads per workgroup, row blocks, head groups
   const uint16_t* q;
   int T, q_pos0;
   const int32_t* table;
@@ -52,7 +61,7 @@ struct PrefillParams {
   int kv_begin, kv_end;
   int causal;
   float scale_log2;
-  int row_tiles;
+  int row_tiles;                         // row tiles of 32 * NR rows
   uint16_t* out;
   float* out_lse;
   float* part_o;
@@ -71,55 +80,57 @@ __device__ __forceinline__ int v_lds_off(int page, int d, int half) {
   return page * 4096 + d * 32 + ((half ^ ((d >> 3) & 1)) << 4);
 }
 
+// Staging: thread tid moves page tid / 128 of the tile, bytes
+// [i*2048 + (tid % 128)*16, +16) of that page's K and of its V (i = 0, 1).
 struct TileRegs {
-  u32x4 k[4];   // this thread's 4 x 16 B of its wave's K page
-  u32x4 v[4];   // and of its V page
+  u32x4 k[2];
+  u32x4 v[2];
+  bool valid;
 };
 
-// Wave w fetches page w of the tile: K page bytes [i*1024 + lane*16), same for V.
-__device__ __forceinline__ void load_tile(TileRegs& r, const PrefillParams& p, int tile, int w,
-                                          int lane, int kvh, bool& valid) {
-  const int lblk = tile * 4 + w;
+__device__ __forceinline__ void load_tile(TileRegs& r, const PrefillParams& p, int tile, int tid,
+                                          int kvh) {
+  const int pg = tid >> 7, t128 = tid & 127;
+  const int lblk = tile * 4 + pg;
   int blk = -1;
   if (lblk < p.maxb && lblk * kBlock < p.kv_end) blk = p.table[lblk];
-  valid = (unsigned)blk < (unsigned)p.num_blocks;
-  if (!valid) return;
+  r.valid = (unsigned)blk < (unsigned)p.num_blocks;
+  if (!r.valid) return;
   const uint8_t* kp = p.k + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * kBlock * D * 2;
   const uint8_t* vp = p.v + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * D * kBlock * 2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r.k[i] = *reinterpret_cast<const u32x4*>(kp + i * 1024 + lane * 16);
-    r.v[i] = *reinterpret_cast<const u32x4*>(vp + i * 1024 + lane * 16);
+  for (int i = 0; i < 2; ++i) {
+    r.k[i] = *reinterpret_cast<const u32x4*>(kp + i * 2048 + t128 * 16);
+    r.v[i] = *reinterpret_cast<const u32x4*>(vp + i * 2048 + t128 * 16);
   }
 }
 
-// Registers -> LDS.  Tokens outside [kv_begin, kv_end) get zero V (and zero K)
-// on boundary tiles, and pages without a valid block are all zero, so masked
+// Registers -> LDS.  Tokens outside [kv_begin, kv_end) get zero K and V on
+// boundary tiles, and pages without a valid block are all zero, so masked
 // positions contribute exactly nothing to P V.
-__device__ __forceinline__ void store_tile(uint8_t* ks, uint8_t* vs, const TileRegs& r,
-                                           const PrefillParams& p, int tile, int w, int lane,
-                                           bool valid, bool boundary) {
-  const int tok_base = tile * BN + w * kBlock;     // first token of this wave's page
+__device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& r, const PrefillParams& p,
+                                           int tile, int tid) {
+  uint8_t* ks = buf;
+  uint8_t* vs = buf + TILE_BYTES;
+  const int pg = tid >> 7, t128 = tid & 127;
+  const int tok_base = tile * BN + pg * kBlock;   // first token of this page
+  const bool boundary = tile * BN < p.kv_begin || tile * BN + BN > p.kv_end;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int o = i * 1024 + lane * 16;
-    // K: token o / 256 of the page, chunk (o % 256) / 16
-    {
+  for (int i = 0; i < 2; ++i) {
+    const int o = i * 2048 + t128 * 16;
+    {  // K: token o / 256 of the page, chunk (o % 256) / 16
       const int tp = o >> 8, c = (o & 255) >> 4;
-      u32x4 val = r.k[i];
-      if (!valid) val = u32x4{0u, 0u, 0u, 0u};
-      else if (boundary) {
+      u32x4 val = r.valid ? r.k[i] : u32x4{0u, 0u, 0u, 0u};
+      if (boundary) {
         const int ta = tok_base + tp;
         if (ta < p.kv_begin || ta >= p.kv_end) val = u32x4{0u, 0u, 0u, 0u};
       }
-      *reinterpret_cast<u32x4*>(ks + k_lds_off(w * kBlock + tp, c)) = val;
+      *reinterpret_cast<u32x4*>(ks + k_lds_off(pg * kBlock + tp, c)) = val;
     }
-    // V: dimension o / 32, tokens 8*th .. 8*th+7 with th = (o % 32) / 16
-    {
+    {  // V: dimension o / 32, tokens 8*th .. 8*th+7 with th = (o % 32) / 16
       const int d = o >> 5, th = (o & 31) >> 4;
-      u32x4 val = r.v[i];
-      if (!valid) val = u32x4{0u, 0u, 0u, 0u};
-      else if (boundary) {
+      u32x4 val = r.valid ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
+      if (boundary) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ta = tok_base + 8 * th + 2 * e;
@@ -138,66 +149,72 @@ __device__ __forceinline__ void store_tile(uint8_t* ks, uint8_t* vs, const TileR
                                                   __uint_as_float(val[e] & 0xffff0000u)));
       // tokens 8th+0..3 -> half 0, tokens 8th+4..7 -> half 1; byte offset 8*th
       const u32x2 lo = {val[0], val[1]}, hi = {val[2], val[3]};
-      *reinterpret_cast<u32x2*>(vs + v_lds_off(w, d, 0) + 8 * th) = lo;
-      *reinterpret_cast<u32x2*>(vs + v_lds_off(w, d, 1) + 8 * th) = hi;
+      *reinterpret_cast<u32x2*>(vs + v_lds_off(pg, d, 0) + 8 * th) = lo;
+      *reinterpret_cast<u32x2*>(vs + v_lds_off(pg, d, 1) + 8 * th) = hi;
     }
   }
 }
 
-// One 64-token K/V tile for this wave's 32 query rows: S^T = K Q^T, online
-// softmax, O^T += V^T P^T.  The per-score visibility test runs only on tiles
-// that cross kv_begin / kv_end or the causal diagonal of this wave's rows
-// (need_mask, uniform over the wave).
 struct RowState {
-  f32x16 o[4];
-  float m, l, mtrue;
+  f32x16 o[4];     // O^T[32*dt + 8*(r/4) + 4*(lane/32) + r%4][row]
+  float m, l;      // running max (log2 units, lazy) and this lane's share of the sum
+  float mtrue;     // this lane's exact max of the scaled scores
 };
 
-template <bool NEG_SCALE>
-__device__ __forceinline__ void attend_tile(RowState& st, const uint8_t* ks, const uint8_t* vs,
-                                            const u32x4 (&qf)[8], const PrefillParams& p, int tb,
-                                            int my_pos, int qr, int hi, bool need_mask) {
-  // ---- S^T = K Q^T over two 32-token halves of the tile
-  f32x16 s[2];
+// S^T for one tile: s[mt][r] = score of key 32*mt + 8*(r/4) + 4*hi + r%4.
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const uint8_t* ks, const u32x4 (&qf)[8],
+                                        int qr, int hi) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-    const int t = 32 * mt + qr;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + k_lds_off(t, 2 * c + hi));
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + k_lds_off(32 * mt + qr, 2 * c + hi));
       s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
                                                      __builtin_bit_cast(bf16x8, qf[c]), s[mt], 0,
                                                      0, 0);
     }
-  }
-  // ---- mask, online softmax in log2 units.  The largest scaled score is
-  // c * max(s) for c > 0 and c * min(s) for c < 0, so the scale is folded
-  // into one FMA per score: p = exp2(s * c - m).
-  const float c = p.scale_log2;
-  const float hidden = NEG_SCALE ? INFINITY : -INFINITY;   // s * c == -inf
-  if (need_mask) {
-    // visible keys of this lane's row: [lo, hi_) relative to the tile
-    const int lo = p.kv_begin - tb - 4 * hi;
-    const int hi_ = (p.causal ? min(p.kv_end, my_pos + 1) : p.kv_end) - tb - 4 * hi;
+}
+
+// Tiles crossing kv_begin / kv_end or this wave's causal diagonal need the
+// per-score visibility test (uniform over the wave).
+__device__ __forceinline__ bool tile_needs_mask(const PrefillParams& p, int tb, int w_minpos) {
+  return tb < p.kv_begin || tb + BN > p.kv_end || (p.causal && tb + BN - 1 > w_minpos);
+}
+
+// Scores of keys this lane's row may not see become the value that scales
+// to -inf.
+template <bool NEG_SCALE>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const PrefillParams& p, int tb,
+                                          int my_pos, int hi) {
+  const float hidden = NEG_SCALE ? INFINITY : -INFINITY;
+  const int lo = p.kv_begin - tb - 4 * hi;
+  const int hi_ = (p.causal ? min(p.kv_end, my_pos + 1) : p.kv_end) - tb - 4 * hi;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ti = 32 * mt + 8 * (r >> 2) + (r & 3);
-        s[mt][r] = (ti >= lo && ti < hi_) ? s[mt][r] : hidden;
-      }
-  }
+    for (int r = 0; r < 16; ++r) {
+      const int ti = 32 * mt + 8 * (r >> 2) + (r & 3);
+      s[mt][r] = (ti >= lo && ti < hi_) ? s[mt][r] : hidden;
+    }
+}
+
+// Running max for a tile's scores, in log2 units with the scale c folded in
+// (the largest scaled score is c * max(s) for c > 0 and c * min(s) for c < 0).
+// The max is raised only when a score exceeds it by more than kLazy, which
+// keeps every weight below 2^kLazy; then the row's lane pair agrees on the new
+// max and O, l are rescaled.  Returns the max to subtract.
+template <bool NEG_SCALE>
+__device__ __forceinline__ float update_max(RowState& st, const f32x16 (&s)[2], float c) {
+  const float hidden = NEG_SCALE ? INFINITY : -INFINITY;
   float ext = hidden;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) ext = NEG_SCALE ? fminf(ext, s[mt][r]) : fmaxf(ext, s[mt][r]);
-  // The running max is raised only when a score exceeds it by more than
-  // kLazy (weights stay below 2^kLazy); the row's lane pair then agrees on the
-  // new max and O, l are rescaled.  Same result, and the common tile needs no
-  // cross-lane step and no rescale.
   const float lmx = ext == hidden ? -INFINITY : ext * c;
   st.mtrue = fmaxf(st.mtrue, lmx);
   if (__ballot(lmx > st.m + kLazy) != 0ull) {
@@ -211,56 +228,78 @@ __device__ __forceinline__ void attend_tile(RowState& st, const uint8_t* ks, con
     for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
     st.m = m_new;
   }
-  const float m_use = st.m == -INFINITY ? 0.f : st.m;
-  // ---- O^T += V^T P^T, four 16-token k-steps, in fp16 (V was converted
-  // exactly when staged; fp16 weights carry 11 significant bits).  The row sum
-  // is taken over the rounded weights that enter the product, so the result
-  // stays an exact weighted average of V rows.
-  float rs = 0.f;
+  return st.m == -INFINITY ? 0.f : st.m;
+}
+
+// One pipelined step of a wave: the scores s_cur of tile j (already masked)
+// become fp16 weights while the K Q^T products of tile j+1 (LDS buffer nxt)
+// run into s_next, then O^T += V^T P^T for tile j.  The row sum is taken over
+// the rounded weights that enter the product, so the result stays an exact
+// weighted average of V rows.
+template <bool NEG_SCALE>
+__device__ __forceinline__ void attend_step(RowState& st, const f32x16 (&s_cur)[2],
+                                            f32x16 (&s_next)[2], const uint8_t* cur,
+                                            const uint8_t* nxt, const u32x4 (&qf)[8], float c,
+                                            int qr, int hi) {
+  const float m_use = update_max<NEG_SCALE>(st, s_cur, c);
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      f16x8 pb;
+    for (int r = 0; r < 16; ++r) s_next[mt][r] = 0.f;
+  f16x8 pb[4];      // k-step ks = 2*mt + rr takes s_cur[mt][8*rr .. 8*rr+7]
+  float rs = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pb[e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][8 * rr + e], c, -m_use));
+  for (int cc = 0; cc < 8; ++cc) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 pr = {pb[2 * e], pb[2 * e + 1]};
-        rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
-      }
-      const int page = 2 * mt + rr;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int d = 32 * dt + qr;
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + v_lds_off(page, d, hi));
-        st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf), pb,
-                                                         st.o[dt], 0, 0, 0);
-      }
+    for (int mt = 0; mt < 2; ++mt) {
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(nxt + k_lds_off(32 * mt + qr, 2 * cc + hi));
+      s_next[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                          __builtin_bit_cast(bf16x8, qf[cc]),
+                                                          s_next[mt], 0, 0, 0);
     }
+    const int kst = cc >> 1, e0 = (cc & 1) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pb[kst][e0 + e] = (_Float16)__builtin_amdgcn_exp2f(
+          __builtin_fmaf(s_cur[kst >> 1][8 * (kst & 1) + e0 + e], c, -m_use));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f16x2 pr = {pb[kst][e0 + 2 * e], pb[kst][e0 + 2 * e + 1]};
+      rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
+    }
+  }
   st.l += rs;
+  const uint8_t* vs = cur + TILE_BYTES;
+#pragma unroll
+  for (int kst = 0; kst < 4; ++kst)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + v_lds_off(kst, 32 * dt + qr, hi));
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf), pb[kst],
+                                                       st.o[dt], 0, 0, 0);
+    }
 }
 
 template <bool NEG_SCALE>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2 * TILE_BYTES];
+__global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;        // lane half
   const int qr = lane & 31;        // query row within the wave
 
-  // workgroup -> (kv head, head in group, row tile); heavier (later) row tiles first
+  // workgroup -> (kv head, head group, row tile); heavier (later) rows first
   const int i = blockIdx.x;
   const int kvh = i % p.hkv;
   const int rest = i / p.hkv;
-  const int gi = rest % p.G;
-  const int rt = p.row_tiles - 1 - rest / p.G;
-  const int h = kvh * p.G + gi;
-  const int row0 = rt * BM;
-  const int wrow0 = row0 + w * ROWS_W;
+  const int hgrp = rest % p.HGR;
+  const int rt = p.row_tiles - 1 - rest / p.HGR;
+  const int h = kvh * p.G + hgrp * p.NH + w % p.NH;
+  const int row0 = rt * ROWS_W * p.NR;
+  const int wrow0 = row0 + (w / p.NH) * ROWS_W;
   const int my_row = wrow0 + qr;
   const bool row_ok = my_row < p.T;
   const int my_pos = p.q_pos0 + my_row;
@@ -276,16 +315,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   }
 
   // keys this workgroup may see
-  const int last_row = min(row0 + BM, p.T) - 1;
+  const int last_row = min(row0 + ROWS_W * p.NR, p.T) - 1;
   int key_end = p.kv_end;
   if (p.causal) key_end = min(key_end, p.q_pos0 + last_row + 1);
   const int t_lo = p.kv_begin / BN;
   const int t_hi = key_end > p.kv_begin ? (key_end - 1) / BN : t_lo - 1;
-  // this wave's rows: position range for masking decisions
-  const int w_last = min(wrow0 + ROWS_W, p.T) - 1;
   const int w_minpos = p.q_pos0 + wrow0;
-  const int w_maxpos = p.q_pos0 + w_last;
-  const bool wave_live = wrow0 < p.T;
 
   RowState st;
 #pragma unroll
@@ -294,46 +329,53 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     for (int r = 0; r < 16; ++r) st.o[dt][r] = 0.f;
   st.m = -INFINITY;
   st.l = 0.f;
-  st.mtrue = -INFINITY;           // this lane's exact max of the scaled scores
+  st.mtrue = -INFINITY;
+  const float c = p.scale_log2;
 
-  TileRegs regs;
-  bool valid = false;
   if (t_lo <= t_hi) {
-    load_tile(regs, p, t_lo, w, lane, kvh, valid);
-    const bool bnd = t_lo * BN < p.kv_begin || t_lo * BN + BN > p.kv_end;
-    store_tile(smem[0], smem[0] + TILE_BYTES, regs, p, t_lo, w, lane, valid, bnd);
-  }
-  __syncthreads();
-
-  for (int tile = t_lo; tile <= t_hi; ++tile) {
-    const int buf = (tile - t_lo) & 1;
-    const bool more = tile < t_hi;
-    if (more) load_tile(regs, p, tile + 1, w, lane, kvh, valid);
-
-    const int tb = tile * BN;
-    const bool wave_sees = wave_live && (!p.causal || tb <= w_maxpos);
-    if (wave_sees) {
-      const uint8_t* ks = smem[buf];
-      const uint8_t* vs = smem[buf] + TILE_BYTES;
-      const bool need_mask = tb < p.kv_begin || tb + BN > p.kv_end ||
-                             (p.causal && tb + BN - 1 > w_minpos);
-      attend_tile<NEG_SCALE>(st, ks, vs, qf, p, tb, my_pos, qr, hi, need_mask);
-    }
-
-    if (more) {
-      const int nb = buf ^ 1;
-      const int nt = tile + 1;
-      const bool bnd = nt * BN < p.kv_begin || nt * BN + BN > p.kv_end;
-      store_tile(smem[nb], smem[nb] + TILE_BYTES, regs, p, nt, w, lane, valid, bnd);
+    TileRegs regs;
+    load_tile(regs, p, t_lo, tid, kvh);
+    store_tile(smem, regs, p, t_lo, tid);
+    if (t_lo + 1 <= t_hi) {
+      load_tile(regs, p, t_lo + 1, tid, kvh);
+      store_tile(smem + BUF_BYTES, regs, p, t_lo + 1, tid);
     }
     __syncthreads();
+
+    f32x16 sa[2], sb[2];
+    qk_tile(sa, smem, qf, qr, hi);
+    if (tile_needs_mask(p, t_lo * BN, w_minpos)) mask_tile<NEG_SCALE>(sa, p, t_lo * BN, my_pos, hi);
+
+    // Tile j lives in ring slot (j - t_lo) % 3.  Step j loads tile j+2 into
+    // registers, attends to tile j while computing the scores of tile j+1
+    // (past the last tile those products read a stale slot and are dropped),
+    // stores tile j+2 into the slot tile j-1 left, and ends on the barrier
+    // that publishes it.
+    int slot = 0;
+    auto step = [&](int j, const f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+      const int s1 = slot == 2 ? 0 : slot + 1;
+      const int s2 = s1 == 2 ? 0 : s1 + 1;
+      const bool prefetch = j + 2 <= t_hi;
+      TileRegs nregs;
+      if (prefetch) load_tile(nregs, p, j + 2, tid, kvh);
+      attend_step<NEG_SCALE>(st, s_cur, s_next, smem + slot * BUF_BYTES, smem + s1 * BUF_BYTES,
+                             qf, c, qr, hi);
+      if (prefetch) store_tile(smem + s2 * BUF_BYTES, nregs, p, j + 2, tid);
+      if (j + 1 <= t_hi && tile_needs_mask(p, (j + 1) * BN, w_minpos))
+        mask_tile<NEG_SCALE>(s_next, p, (j + 1) * BN, my_pos, hi);
+      slot = s1;
+      __syncthreads();
+    };
+    for (int j = t_lo; j <= t_hi; j += 2) {
+      step(j, sa, sb);
+      if (j + 1 <= t_hi) step(j + 1, sb, sa);
+    }
   }
 
   // ---- epilogue: row sum over the lane pair, then normalise or emit partials
   float l = st.l + __shfl_xor(st.l, 32);
   const float mtrue = fmaxf(st.mtrue, __shfl_xor(st.mtrue, 32));
   float m = st.m;
-  f32x16 (&o)[4] = st.o;
   if (!row_ok) return;
   const bool empty = !(l > 0.f);
   const int64_t ro = (int64_t)my_row * p.hq + h;
@@ -346,10 +388,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * dt + 8 * j + 4 * hi;
         u32x2 pk;
-        pk.x = (uint32_t)f32_to_bf16_bits(o[dt][4 * j] * inv) |
-               ((uint32_t)f32_to_bf16_bits(o[dt][4 * j + 1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16_bits(o[dt][4 * j + 2] * inv) |
-               ((uint32_t)f32_to_bf16_bits(o[dt][4 * j + 3] * inv) << 16);
+        pk.x = (uint32_t)f32_to_bf16_bits(st.o[dt][4 * j] * inv) |
+               ((uint32_t)f32_to_bf16_bits(st.o[dt][4 * j + 1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(st.o[dt][4 * j + 2] * inv) |
+               ((uint32_t)f32_to_bf16_bits(st.o[dt][4 * j + 3] * inv) << 16);
         *reinterpret_cast<u32x2*>(op + d) = pk;
       }
     if (p.out_lse && hi == 0) p.out_lse[ro] = empty ? -INFINITY : m * kLn2 + logf(l);
@@ -358,8 +400,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     const float f = empty ? 0.f : __builtin_amdgcn_exp2f(m - mtrue);
     l *= f;
     m = mtrue;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] *= f;
     float* op = p.part_o + ro * D;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -367,8 +407,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * dt + 8 * j + 4 * hi;
         const f32x4 val = empty ? f32x4{0.f, 0.f, 0.f, 0.f}
-                                : f32x4{o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2],
-                                        o[dt][4 * j + 3]};
+                                : f32x4{st.o[dt][4 * j] * f, st.o[dt][4 * j + 1] * f,
+                                        st.o[dt][4 * j + 2] * f, st.o[dt][4 * j + 3] * f};
         *reinterpret_cast<f32x4*>(op + d) = val;
       }
     if (hi == 0) {
@@ -376,6 +416,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       p.part_l[ro] = empty ? 0.f : l;
     }
   }
+}
+
+int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+
+// 96 KiB of dynamic LDS needs an explicit opt-in per kernel (once per process
+// and device is enough; repeating it is harmless).
+template <bool NEG>
+hipError_t launch_one(const PrefillParams& p, unsigned wgs, hipStream_t s) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NEG>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prefill_kernel<NEG>, dim3(wgs), dim3(NTHREADS), LDS_BYTES, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -393,6 +446,9 @@ hipError_t launch_prefill(const CacheView& c, const void* q, int T, int hq, int 
   p.hkv = c.hkv;
   p.hq = hq;
   p.G = hq / c.hkv;
+  p.NH = gcd(p.G, NWAVE);
+  p.NR = NWAVE / p.NH;
+  p.HGR = p.G / p.NH;
   p.q = static_cast<const uint16_t*>(q);
   p.T = T;
   p.q_pos0 = q_pos0;
@@ -402,19 +458,16 @@ hipError_t launch_prefill(const CacheView& c, const void* q, int T, int hq, int 
   p.kv_end = kv_end;
   p.causal = causal;
   p.scale_log2 = scale * kLog2e;
-  p.row_tiles = (T + BM - 1) / BM;
+  p.row_tiles = (T + ROWS_W * p.NR - 1) / (ROWS_W * p.NR);
   p.out = static_cast<uint16_t*>(out);
   p.out_lse = out_lse;
   p.part_o = part_o;
   p.part_m = part_m;
   p.part_l = part_l;
-  const int64_t wgs = (int64_t)p.row_tiles * hq;
+  const int64_t wgs = (int64_t)p.row_tiles * c.hkv * p.HGR;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-  if (scale < 0.f)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)wgs), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)wgs), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return scale < 0.f ? launch_one<true>(p, (unsigned)wgs, s)
+                     : launch_one<false>(p, (unsigned)wgs, s);
 }
 
 }  // namespace pkv
