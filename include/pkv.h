@@ -83,7 +83,15 @@ enum {
  * lets K and V share one interleaved allocation.  Pools must be 16-byte
  * aligned and block_stride*elem_size a multiple of 16.
  * E4M3 caches carry fp32 scales k_scale/v_scale [num_blocks][num_kv_heads]:
- * element value = decode(code) * scale of its (block, head); otherwise NULL. */
+ * element value = decode(code) * scale of its (block, head); otherwise NULL.
+ * E4M3 pages (16*head_dim bytes each, same places) hold their codes in the
+ * order the decode kernel's matrix instructions consume them, so that each
+ * 64-lane load reads 1 KiB of contiguous memory.  Byte offsets in a page:
+ *   K(token t, dim d): (c>>1)*1024 + ((g<<4) + t)*16 + (c&1)*8 + (d&7),
+ *                      c = d>>5, g = (d>>3)&3;
+ *   V(token t, dim d): (n>>2)*1024 + (((t>>2)<<4) + (d&15))*16 + (n&3)*4 + (t&3),
+ *                      n = d>>4.
+ * pkv_kv_append writes this order; callers treat the pages as opaque. */
 typedef struct pkv_cache_desc {
   void* k_cache;
   void* v_cache;

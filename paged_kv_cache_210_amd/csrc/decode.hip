@@ -175,20 +175,32 @@ __device__ __forceinline__ void compute_page(SoftState<D>& st, const BF16Page<D>
 }
 
 // ---- E4M3 pages ---------------------------------------------------------------
+// E4M3 pages are stored in fragment order (kv_append writes them so): lane l's
+// codes for the whole page are 16-byte pieces at i*1024 + 16*l, so every load
+// instruction reads 1 KiB of contiguous memory.  K piece i holds the score
+// product's fragments c = 2i, 2i+1 (8 codes each: K[t = l%16][32c + 8*(l/16)
+// .. +8]); V piece j holds the PV fragments nn = 4j .. 4j+3 (4 codes each:
+// V^T[16nn + l%16][4*(l/16) .. +4]).
 template <int D>
 struct FP8Page {
-  u32x2 k[D / 32];     // 8 codes: K[t = l%16][32c + 8*(l/16) .. +8]
-  uint32_t v[D / 16];  // 4 codes: V^T[16n + l%16][4*(l/16) .. +4]
+  u32x4 k[D / 64];
+  u32x4 v[D / 64];
   float ks, vs;        // scales of this (block, head)
+  __device__ __forceinline__ u32x2 kfrag(int c) const {
+    const u32x4& q = k[c >> 1];
+    return (c & 1) ? u32x2{q.z, q.w} : u32x2{q.x, q.y};
+  }
+  __device__ __forceinline__ uint32_t vfrag(int nn) const { return v[nn >> 2][nn & 3]; }
 };
 
 template <int D>
 __device__ __forceinline__ void load_page(FP8Page<D>& pg, const uint8_t* kp, const uint8_t* vp,
                                           int col, int grp) {
+  const int lane = grp * 16 + col;
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) pg.k[c] = stream_load<u32x2>(kp + col * D + 32 * c + 8 * grp);
+  for (int i = 0; i < D / 64; ++i) pg.k[i] = stream_load<u32x4>(kp + i * 1024 + lane * 16);
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n) pg.v[n] = stream_load<uint32_t>(vp + (16 * n + col) * 16 + 4 * grp);
+  for (int i = 0; i < D / 64; ++i) pg.v[i] = stream_load<u32x4>(vp + i * 1024 + lane * 16);
 }
 
 // E4M3 -> fp16 with the gfx950 scaled convert at scale 1: every finite E4M3
@@ -216,7 +228,7 @@ __device__ __forceinline__ void compute_page(SoftState<D>& st, const FP8Page<D>&
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16(pg.k[c]),
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16(pg.kfrag(c)),
                                               __builtin_bit_cast(f16x8, qf[c]), s, 0, 0, 0);
   const int vc = valid_count(tok, n);
   const float kf = sl2 * pg.ks;
@@ -233,7 +245,7 @@ __device__ __forceinline__ void compute_page(SoftState<D>& st, const FP8Page<D>&
   f32x4 t[D / 16];     // one product per tile, so the MFMAs issue back to back
 #pragma unroll
   for (int nn = 0; nn < D / 16; ++nn)
-    t[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_f16(pg.v[nn] & keep), pb, zero, 0, 0,
+    t[nn] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_f16(pg.vfrag(nn) & keep), pb, zero, 0, 0,
                                                  0);
 #pragma unroll
   for (int nn = 0; nn < D / 16; ++nn) st.o[nn] += t[nn] * vf;
@@ -253,9 +265,11 @@ __device__ __forceinline__ bool issue_page(PageT<D, KVF>& pg, const DecodeParams
   load_page<D>(pg, kp, vp, col, grp);
   if constexpr (KVF == PKV_FP8_E4M3) {
     // vector loads (the address is forced into a VGPR), so the scales are
-    // ordered with the page loads instead of waiting on the scalar queue
-    const float* ks = p.k_scale + (int64_t)(ok ? blk : 0) * p.hkv + kvh;
-    const float* vs = p.v_scale + (int64_t)(ok ? blk : 0) * p.hkv + kvh;
+    // ordered with the page loads instead of waiting on the scalar queue;
+    // global (not generic) pointers, so they are counted like the page loads
+    typedef const __attribute__((address_space(1))) float gfloat_t;
+    gfloat_t* ks = (gfloat_t*)(p.k_scale + (int64_t)(ok ? blk : 0) * p.hkv + kvh);
+    gfloat_t* vs = (gfloat_t*)(p.v_scale + (int64_t)(ok ? blk : 0) * p.hkv + kvh);
     asm volatile("" : "+v"(ks), "+v"(vs));
     pg.ks = *ks;
     pg.vs = *vs;
@@ -407,13 +421,9 @@ __global__ __launch_bounds__(kThreads, 3) void decode_mfma_kernel(DecodeParams p
 // (partition, kv head, sequence); heads of the group one after another.
 template <int QT, int KT>
 __device__ __forceinline__ float kv_value(const uint8_t* base, int64_t idx) {
+  static_assert(KT == PKV_F32 || KT == PKV_BF16, "E4M3 pools take the MFMA path");
   if constexpr (KT == PKV_F32) return reinterpret_cast<const float*>(base)[idx];
-  else if constexpr (KT == PKV_BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
-  else {
-    const uint32_t c = base[idx];
-    const uint32_t h = ((c & 0x7fu) << 7) | ((c & 0x80u) << 8);
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)h) * 256.f;
-  }
+  else return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
 }
 
 template <int QT, int KT>
@@ -444,11 +454,6 @@ __global__ __launch_bounds__(64) void decode_simple_kernel(DecodeParams p, int D
       if ((unsigned)blk >= (unsigned)p.num_blocks) continue;
       const uint8_t* kp = p.k + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * kBlock * D * esz;
       const uint8_t* vp = p.v + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * D * kBlock * esz;
-      float ks = 1.f, vs = 1.f;
-      if constexpr (KT == PKV_FP8_E4M3) {
-        ks = p.k_scale[(int64_t)blk * p.hkv + kvh];
-        vs = p.v_scale[(int64_t)blk * p.hkv + kvh];
-      }
       for (int t = 0; t < kBlock && j * kBlock + t < n; ++t) {
         float part_dot = 0.f;
 #pragma unroll
@@ -456,7 +461,7 @@ __global__ __launch_bounds__(64) void decode_simple_kernel(DecodeParams p, int D
           const int d = lane + 64 * e;
           if (d < D) part_dot += q[e] * kv_value<QT, KT>(kp, t * D + d);
         }
-        const float s = wave_sum(part_dot) * ks * p.scale_log2;
+        const float s = wave_sum(part_dot) * p.scale_log2;
         const float m_new = fmaxf(m, s);
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         const float pw = __builtin_amdgcn_exp2f(s - m_new);
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(64) void decode_simple_kernel(DecodeParams p, int D
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int d = lane + 64 * e;
-          const float vv = d < D ? kv_value<QT, KT>(vp, d * kBlock + t) * vs : 0.f;
+          const float vv = d < D ? kv_value<QT, KT>(vp, d * kBlock + t) : 0.f;
           o[e] = o[e] * alpha + pw * vv;
         }
         m = m_new;

@@ -77,6 +77,17 @@ __device__ __forceinline__ float chunk_f32(const u32x4& x0, const u32x4* x, int 
   }
 }
 
+// E4M3 pages are stored in the order the decode MFMAs consume them (the
+// layout pkv.h documents): byte offsets within a (block, head) page.
+__device__ __forceinline__ int e4m3_k_off(int t, int d) {
+  const int c = d >> 5, grp = (d >> 3) & 3;
+  return (c >> 1) * 1024 + ((grp << 4) + t) * 16 + (c & 1) * 8 + (d & 7);
+}
+__device__ __forceinline__ int e4m3_v_off(int t, int d) {
+  const int nn = d >> 4;
+  return (nn >> 2) * 1024 + (((t >> 2) << 4) + (d & 15)) * 16 + (nn & 3) * 4 + (t & 3);
+}
+
 template <int SRC, int DST>
 __device__ __forceinline__ void store_chunk(const AppendParams& p, const SrcChunk<SRC>& c,
                                             int blk, int64_t base, int off, int e) {
@@ -85,6 +96,9 @@ __device__ __forceinline__ void store_chunk(const AppendParams& p, const SrcChun
   const int64_t kd = base + (int64_t)h * kBlock * p.D + (int64_t)off * p.D + d;
   const int64_t vd = base + (int64_t)h * p.D * kBlock + (int64_t)d * kBlock + off;
   if constexpr (DST == PKV_FP8_E4M3) {
+    // the 8 codes of a chunk stay contiguous in the K page (d % 8 == 0)
+    const int64_t kq = base + (int64_t)h * kBlock * p.D + e4m3_k_off(off, d);
+    const int64_t vq = base + (int64_t)h * p.D * kBlock;
     const int64_t si = (int64_t)blk * p.hkv + h;
     const float inv_k = __frcp_rn(p.k_scale[si]);
     const float inv_v = __frcp_rn(p.v_scale[si]);
@@ -104,9 +118,9 @@ __device__ __forceinline__ void store_chunk(const AppendParams& p, const SrcChun
       const uint32_t ck = e4m3_encode(__fmul_rn(chunk_f32<SRC>(k0, kx, i), inv_k));
       codes[i >> 2] |= ck << (8 * (i & 3));
       const uint32_t cv = e4m3_encode(__fmul_rn(chunk_f32<SRC>(v0, vx, i), inv_v));
-      p.v_pool[vd + (int64_t)i * kBlock] = (uint8_t)cv;
+      p.v_pool[vq + e4m3_v_off(off, d + i)] = (uint8_t)cv;
     }
-    *reinterpret_cast<u32x2*>(p.k_pool + kd) = codes;
+    *reinterpret_cast<u32x2*>(p.k_pool + kq) = codes;
   } else if constexpr (DST == PKV_BF16) {
     *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.k_pool) + kd) = c.k;
     uint16_t* vp = reinterpret_cast<uint16_t*>(p.v_pool) + vd;

@@ -36,6 +36,22 @@ def kv_elements(t, fmt):
     return t.detach().cpu().numpy()
 
 
+def e4m3_pages_logical(k_phys, v_phys):
+    """E4M3 pool bytes in the fragment order include/pkv.h documents -> logical
+    code arrays K [..., 16, d] and V [..., d, 16] (the oracle's layout)."""
+    k_phys, v_phys = np.asarray(k_phys), np.asarray(v_phys)
+    nb, hkv, _, D = k_phys.shape
+    t = np.arange(16)[:, None]
+    d = np.arange(D)[None, :]
+    c, grp, nn = d >> 5, (d >> 3) & 3, d >> 4
+    koff = (c >> 1) * 1024 + ((grp << 4) + t) * 16 + (c & 1) * 8 + (d & 7)              # [t, d]
+    voff = (nn >> 2) * 1024 + (((t >> 2) << 4) + (d & 15)) * 16 + (nn & 3) * 4 + (t & 3)  # [t, d]
+    assert len(np.unique(koff)) == 16 * D and len(np.unique(voff)) == 16 * D
+    kf = k_phys.reshape(nb, hkv, 16 * D)
+    vf = v_phys.reshape(nb, hkv, 16 * D)
+    return kf[:, :, koff], vf[:, :, voff].transpose(0, 1, 3, 2)
+
+
 def q_elements(t):
     return (bits(t), "bf16") if t.dtype == torch.bfloat16 else (t.detach().cpu().numpy(), "f32")
 

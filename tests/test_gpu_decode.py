@@ -9,8 +9,8 @@ import torch
 
 from oracle import pkv_oracle as O
 import synth
-from tests._util import (TOL, bits, compare_rows, gpu_cache, oracle_cache, q_elements,
-                         kv_elements)
+from tests._util import (TOL, bits, compare_rows, e4m3_pages_logical, gpu_cache, kv_elements,
+                         oracle_cache, q_elements)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -61,6 +61,8 @@ def _pool_equal(cache, oc, blocks=None):
     gv = cache.v.cpu()
     if oc.fmt == "bf16":
         gk, gv = bits(gk), bits(gv)
+    elif oc.fmt == "e4m3":
+        gk, gv = e4m3_pages_logical(gk.numpy(), gv.numpy())
     else:
         gk, gv = gk.numpy(), gv.numpy()
     if blocks is not None:
