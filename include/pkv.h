@@ -73,25 +73,27 @@ enum {
 #define PKV_SCALE_GROUP 64  /* tokens per FP8 scale [P2 3.2]              */
 
 /* ---- paged KV cache of one attention layer [P1 2.2, P2 3.1] -------------
- * Physical block b, kv head h:
- *   K page at k_cache + b*block_stride + h*16*head_dim elements, laid out
- *     [16 tokens][head_dim]   (token-major: one token's key is contiguous);
- *   V page at v_cache + b*block_stride + h*head_dim*16 elements, laid out
- *     [head_dim][16 tokens]   (dimension-major: one dimension's 16 values are
- *     contiguous).
+ * Physical block b, kv head h: the K page starts at
+ *   k_cache + b*block_stride + h*16*head_dim elements,
+ * and the V page at
+ *   v_cache + b*block_stride + h*head_dim*16 elements.
+ * Each page holds the 16 tokens x head_dim elements of that (block, head).
  * block_stride >= num_kv_heads*16*head_dim, counted in elements of kv_dtype,
  * lets K and V share one interleaved allocation.  Pools must be 16-byte
  * aligned and block_stride*elem_size a multiple of 16.
+ * Order of the elements inside a page:
+ *   PKV_F32: K [16 tokens][head_dim], V [head_dim][16 tokens].
+ *   PKV_BF16, PKV_FP8_E4M3 ("fragment order"): the order in which the decode
+ *   kernel's matrix instructions consume them, so that each 64-lane load
+ *   reads 1 KiB of contiguous memory.  With e = element bytes (2 or 1),
+ *   byte offsets of token t, dimension d are
+ *     K: (c/(2/e))*1024 + ((g<<4) + t)*16 + (c%(2/e))*8*e + (d&7)*e,
+ *        c = d>>5, g = (d>>3)&3;
+ *     V: (n/(4/e))*1024 + (((t>>2)<<4) + (d&15))*16 + (n%(4/e))*4*e + (t&3)*e,
+ *        n = d>>4.
+ * pkv_kv_append writes these orders; callers treat pages as opaque.
  * E4M3 caches carry fp32 scales k_scale/v_scale [num_blocks][num_kv_heads]:
- * element value = decode(code) * scale of its (block, head); otherwise NULL.
- * E4M3 pages (16*head_dim bytes each, same places) hold their codes in the
- * order the decode kernel's matrix instructions consume them, so that each
- * 64-lane load reads 1 KiB of contiguous memory.  Byte offsets in a page:
- *   K(token t, dim d): (c>>1)*1024 + ((g<<4) + t)*16 + (c&1)*8 + (d&7),
- *                      c = d>>5, g = (d>>3)&3;
- *   V(token t, dim d): (n>>2)*1024 + (((t>>2)<<4) + (d&15))*16 + (n&3)*4 + (t&3),
- *                      n = d>>4.
- * pkv_kv_append writes this order; callers treat the pages as opaque. */
+ * element value = decode(code) * scale of its (block, head); otherwise NULL. */
 typedef struct pkv_cache_desc {
   void* k_cache;
   void* v_cache;

@@ -19,9 +19,9 @@
 // One wave owns one page (16 tokens) per step.  Lane l holds token 4*(l/16)+i
 // (i < 4) of the page for query head l%16: that is both the output layout of
 // the score product and the B-operand layout of the PV product, so softmax
-// weights never leave their lane.  K pages are token-major ([16][d]); V pages
-// are dimension-major ([d][16]) so each lane's four tokens of one dimension are
-// 8 contiguous bytes (4 for E4M3).
+// weights never leave their lane.  bf16 and E4M3 pages are stored in fragment
+// order (each lane's operands for a whole page are contiguous 16-byte pieces,
+// and one load instruction reads 1 KiB of contiguous memory).
 #include <type_traits>
 
 #include "pkv_common.h"
@@ -105,10 +105,16 @@ __device__ __forceinline__ int valid_count(int tok, int n) {
 }
 
 // ---- bf16 pages ---------------------------------------------------------------
+// Pages are in fragment order (pkv_common.h: frag_k_off / frag_v_off), so each
+// of a lane's loads is the 16-byte piece at j*1024 + 16*l.
 template <int D>
 struct BF16Page {
-  u32x4 k[D / 32];     // K[t = l%16][32c + 8*(l/16) .. +8]
-  u32x2 v[D / 16];     // V^T[16n + l%16][4*(l/16) .. +4]
+  u32x4 k[D / 32];     // piece c: K[t = l%16][32c + 8*(l/16) .. +8]
+  u32x4 v[D / 32];     // piece j: V^T[16n + l%16][4*(l/16) .. +4] for n = 2j, 2j+1
+  __device__ __forceinline__ u32x2 vfrag(int n) const {
+    const u32x4& q = v[n >> 1];
+    return (n & 1) ? u32x2{q.z, q.w} : u32x2{q.x, q.y};
+  }
 };
 
 // K/V pages are read once per step: streaming loads (non-temporal when
@@ -125,11 +131,11 @@ __device__ __forceinline__ T stream_load(const uint8_t* p) {
 template <int D>
 __device__ __forceinline__ void load_page(BF16Page<D>& pg, const uint8_t* kp, const uint8_t* vp,
                                           int col, int grp) {
+  const int lane = grp * 16 + col;
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) pg.k[c] = stream_load<u32x4>(kp + 2 * (col * D + 32 * c + 8 * grp));
+  for (int c = 0; c < D / 32; ++c) pg.k[c] = stream_load<u32x4>(kp + c * 1024 + lane * 16);
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n)
-    pg.v[n] = stream_load<u32x2>(vp + 2 * ((16 * n + col) * 16 + 4 * grp));
+  for (int j = 0; j < D / 32; ++j) pg.v[j] = stream_load<u32x4>(vp + j * 1024 + lane * 16);
 }
 
 template <int D>
@@ -162,25 +168,23 @@ __device__ __forceinline__ void compute_page(SoftState<D>& st, const BF16Page<D>
                 vc >= 4 ? 0xffffffffu : (vc == 3 ? 0x0000ffffu : 0u)};
 #pragma unroll
   for (int nn = 0; nn < D / 16; ++nn) {
-    const u32x2 vv = pg.v[nn] & keep;
+    const u32x2 vv = pg.vfrag(nn) & keep;
     st.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb_hi,
                                                         st.o[nn], 0, 0, 0);
   }
 #pragma unroll
   for (int nn = 0; nn < D / 16; ++nn) {
-    const u32x2 vv = pg.v[nn] & keep;
+    const u32x2 vv = pg.vfrag(nn) & keep;
     st.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb_lo,
                                                         st.o[nn], 0, 0, 0);
   }
 }
 
 // ---- E4M3 pages ---------------------------------------------------------------
-// E4M3 pages are stored in fragment order (kv_append writes them so): lane l's
-// codes for the whole page are 16-byte pieces at i*1024 + 16*l, so every load
-// instruction reads 1 KiB of contiguous memory.  K piece i holds the score
-// product's fragments c = 2i, 2i+1 (8 codes each: K[t = l%16][32c + 8*(l/16)
-// .. +8]); V piece j holds the PV fragments nn = 4j .. 4j+3 (4 codes each:
-// V^T[16nn + l%16][4*(l/16) .. +4]).
+// Fragment order as for bf16: K piece i holds the score product's fragments
+// c = 2i, 2i+1 (8 codes each: K[t = l%16][32c + 8*(l/16) .. +8]); V piece j
+// holds the PV fragments nn = 4j .. 4j+3 (4 codes each: V^T[16nn + l%16]
+// [4*(l/16) .. +4]).
 template <int D>
 struct FP8Page {
   u32x4 k[D / 64];
@@ -419,11 +423,19 @@ __global__ __launch_bounds__(kThreads, 3) void decode_mfma_kernel(DecodeParams p
 
 // ---- simple path: any supported dtype pair, vector ALU, one wave per
 // (partition, kv head, sequence); heads of the group one after another.
-template <int QT, int KT>
-__device__ __forceinline__ float kv_value(const uint8_t* base, int64_t idx) {
+// Element (token t, dimension d) of a K page / V page: f32 pages are plain
+// ([16][D] and [D][16]); bf16 pages are in fragment order.
+template <int KT>
+__device__ __forceinline__ float k_value(const uint8_t* page, int t, int d, int D) {
   static_assert(KT == PKV_F32 || KT == PKV_BF16, "E4M3 pools take the MFMA path");
-  if constexpr (KT == PKV_F32) return reinterpret_cast<const float*>(base)[idx];
-  else return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+  if constexpr (KT == PKV_F32) return reinterpret_cast<const float*>(page)[t * D + d];
+  else return bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(page + frag_k_off<2>(t, d)));
+}
+template <int KT>
+__device__ __forceinline__ float v_value(const uint8_t* page, int t, int d) {
+  static_assert(KT == PKV_F32 || KT == PKV_BF16, "E4M3 pools take the MFMA path");
+  if constexpr (KT == PKV_F32) return reinterpret_cast<const float*>(page)[d * kBlock + t];
+  else return bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(page + frag_v_off<2>(t, d)));
 }
 
 template <int QT, int KT>
@@ -459,7 +471,7 @@ __global__ __launch_bounds__(64) void decode_simple_kernel(DecodeParams p, int D
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int d = lane + 64 * e;
-          if (d < D) part_dot += q[e] * kv_value<QT, KT>(kp, t * D + d);
+          if (d < D) part_dot += q[e] * k_value<KT>(kp, t, d, D);
         }
         const float s = wave_sum(part_dot) * p.scale_log2;
         const float m_new = fmaxf(m, s);
@@ -469,7 +481,7 @@ __global__ __launch_bounds__(64) void decode_simple_kernel(DecodeParams p, int D
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int d = lane + 64 * e;
-          const float vv = d < D ? kv_value<QT, KT>(vp, d * kBlock + t) : 0.f;
+          const float vv = d < D ? v_value<KT>(vp, t, d) : 0.f;
           o[e] = o[e] * alpha + pw * vv;
         }
         m = m_new;

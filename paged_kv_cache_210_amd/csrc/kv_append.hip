@@ -34,10 +34,12 @@ __device__ __forceinline__ T load_elem(const void* p, int64_t i) {
 // One wave per token, four tokens per 256-thread workgroup.  Lane chunks are
 // 8 consecutive elements of the token's [Hkv][d] row; each lane issues all of
 // its loads before any store, so a small append (one token per sequence in a
-// decode step) costs about one memory round trip.  K rows are contiguous in a
-// page (one 8-element store per chunk); V elements of one token are 16 apart.
-// Same-type caches copy raw bits; E4M3 caches quantise f32(x) * f32(1/scale)
-// with the scale of the destination (block, head).
+// decode step) costs about one memory round trip.  A chunk's 8 K elements
+// stay contiguous in the page (one store); its V elements are scattered (one
+// store each).  bf16 and E4M3 pages are written in fragment order, f32 pages
+// plainly ([16][d] K, [d][16] V).  Same-type caches copy raw bits; E4M3 caches
+// quantise f32(x) * f32(1/scale) with the scale of the destination
+// (block, head).
 constexpr int kChunk = 8;      // elements per lane chunk
 constexpr int kUnroll = 4;     // chunks in flight per lane
 
@@ -77,27 +79,15 @@ __device__ __forceinline__ float chunk_f32(const u32x4& x0, const u32x4* x, int 
   }
 }
 
-// E4M3 pages are stored in the order the decode MFMAs consume them (the
-// layout pkv.h documents): byte offsets within a (block, head) page.
-__device__ __forceinline__ int e4m3_k_off(int t, int d) {
-  const int c = d >> 5, grp = (d >> 3) & 3;
-  return (c >> 1) * 1024 + ((grp << 4) + t) * 16 + (c & 1) * 8 + (d & 7);
-}
-__device__ __forceinline__ int e4m3_v_off(int t, int d) {
-  const int nn = d >> 4;
-  return (nn >> 2) * 1024 + (((t >> 2) << 4) + (d & 15)) * 16 + (nn & 3) * 4 + (t & 3);
-}
-
 template <int SRC, int DST>
 __device__ __forceinline__ void store_chunk(const AppendParams& p, const SrcChunk<SRC>& c,
                                             int blk, int64_t base, int off, int e) {
   const int h = e / p.D;
   const int d = e - h * p.D;                 // chunk never crosses a head (D % 8 == 0)
-  const int64_t kd = base + (int64_t)h * kBlock * p.D + (int64_t)off * p.D + d;
-  const int64_t vd = base + (int64_t)h * p.D * kBlock + (int64_t)d * kBlock + off;
   if constexpr (DST == PKV_FP8_E4M3) {
-    // the 8 codes of a chunk stay contiguous in the K page (d % 8 == 0)
-    const int64_t kq = base + (int64_t)h * kBlock * p.D + e4m3_k_off(off, d);
+    // bf16 and E4M3 pages are in fragment order (frag_k_off / frag_v_off);
+    // the 8 elements of a chunk stay contiguous in the K page (d % 8 == 0)
+    const int64_t kq = base + (int64_t)h * kBlock * p.D + frag_k_off<1>(off, d);
     const int64_t vq = base + (int64_t)h * p.D * kBlock;
     const int64_t si = (int64_t)blk * p.hkv + h;
     const float inv_k = __frcp_rn(p.k_scale[si]);
@@ -118,16 +108,20 @@ __device__ __forceinline__ void store_chunk(const AppendParams& p, const SrcChun
       const uint32_t ck = e4m3_encode(__fmul_rn(chunk_f32<SRC>(k0, kx, i), inv_k));
       codes[i >> 2] |= ck << (8 * (i & 3));
       const uint32_t cv = e4m3_encode(__fmul_rn(chunk_f32<SRC>(v0, vx, i), inv_v));
-      p.v_pool[vq + e4m3_v_off(off, d + i)] = (uint8_t)cv;
+      p.v_pool[vq + frag_v_off<1>(off, d + i)] = (uint8_t)cv;
     }
     *reinterpret_cast<u32x2*>(p.k_pool + kq) = codes;
   } else if constexpr (DST == PKV_BF16) {
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.k_pool) + kd) = c.k;
-    uint16_t* vp = reinterpret_cast<uint16_t*>(p.v_pool) + vd;
+    uint8_t* kpg = p.k_pool + 2 * (base + (int64_t)h * kBlock * p.D);
+    uint8_t* vpg = p.v_pool + 2 * (base + (int64_t)h * p.D * kBlock);
+    *reinterpret_cast<u32x4*>(kpg + frag_k_off<2>(off, d)) = c.k;
 #pragma unroll
     for (int i = 0; i < kChunk; ++i)
-      vp[(int64_t)i * kBlock] = (uint16_t)((i & 1) ? (c.v[i >> 1] >> 16) : (c.v[i >> 1] & 0xffffu));
+      *reinterpret_cast<uint16_t*>(vpg + frag_v_off<2>(off, d + i)) =
+          (uint16_t)((i & 1) ? (c.v[i >> 1] >> 16) : (c.v[i >> 1] & 0xffffu));
   } else {
+    const int64_t kd = base + (int64_t)h * kBlock * p.D + (int64_t)off * p.D + d;
+    const int64_t vd = base + (int64_t)h * p.D * kBlock + (int64_t)d * kBlock + off;
     float* kp = reinterpret_cast<float*>(p.k_pool) + kd;
     *reinterpret_cast<u32x4*>(kp) = c.k[0];
     *reinterpret_cast<u32x4*>(kp + 4) = c.k[1];

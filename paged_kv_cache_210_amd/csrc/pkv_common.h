@@ -56,6 +56,28 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | code;
 }
 
+// Fragment-order pages (bf16 and E4M3 pools): byte offset of the element of
+// token t, dimension d inside one (block, kv head) page of ES-byte elements.
+// Lane l = 16*g + i of a decode wave finds all of its matrix-instruction
+// fragments in the 16-byte pieces at j*1024 + 16*l (j = 0, 1, ...), so every
+// 64-lane load of a page reads 1 KiB of contiguous memory.
+//   K: the 8 elements K[t][32c + 8g .. +8] (A operand of the score product
+//      for token t = i); a 16-byte piece holds 2/ES of these groups.
+//   V: the 4 elements V[4g .. 4g+4][16n + i] (A operand of the PV product for
+//      dimension 16n + i); a 16-byte piece holds 4/ES of these groups.
+template <int ES>
+__host__ __device__ __forceinline__ int frag_k_off(int t, int d) {
+  constexpr int CPP = 2 / ES;
+  const int c = d >> 5, g = (d >> 3) & 3;
+  return (c / CPP) * 1024 + ((g << 4) + t) * 16 + (c % CPP) * 8 * ES + (d & 7) * ES;
+}
+template <int ES>
+__host__ __device__ __forceinline__ int frag_v_off(int t, int d) {
+  constexpr int NPP = 4 / ES;
+  const int n = d >> 4;
+  return (n / NPP) * 1024 + (((t >> 2) << 4) + (d & 15)) * 16 + (n % NPP) * 4 * ES + (t & 3) * ES;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;

@@ -105,9 +105,14 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const PrefillParams& p, i
   }
 }
 
-// Registers -> LDS.  Tokens outside [kv_begin, kv_end) get zero K and V on
-// boundary tiles, and pages without a valid block are all zero, so masked
-// positions contribute exactly nothing to P V.
+// Registers -> LDS.  Pool pages are in fragment order (pkv_common.h), so a
+// 16-byte piece at byte o of a page holds, with c = o / 1024 and lane
+// l = (o / 16) % 64 = 16g + i:
+//   K: the 8 dimensions 32c + 8g .. +8 of token i;
+//   V: tokens 4g .. 4g+3 of dimensions 32c + i and 32c + 16 + i.
+// Tokens outside [kv_begin, kv_end) get zero K and V on boundary tiles, and
+// pages without a valid block are all zero, so masked positions contribute
+// exactly nothing to P V.
 __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& r, const PrefillParams& p,
                                            int tile, int tid) {
   uint8_t* ks = buf;
@@ -118,22 +123,21 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& r, cons
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int o = i * 2048 + t128 * 16;
-    {  // K: token o / 256 of the page, chunk (o % 256) / 16
-      const int tp = o >> 8, c = (o & 255) >> 4;
+    const int c = o >> 10, l = (o >> 4) & 63, g = l >> 4, li = l & 15;
+    {  // K: token li, chunk 4c + g
       u32x4 val = r.valid ? r.k[i] : u32x4{0u, 0u, 0u, 0u};
       if (boundary) {
-        const int ta = tok_base + tp;
+        const int ta = tok_base + li;
         if (ta < p.kv_begin || ta >= p.kv_end) val = u32x4{0u, 0u, 0u, 0u};
       }
-      *reinterpret_cast<u32x4*>(ks + k_lds_off(pg * kBlock + tp, c)) = val;
+      *reinterpret_cast<u32x4*>(ks + k_lds_off(pg * kBlock + li, 4 * c + g)) = val;
     }
-    {  // V: dimension o / 32, tokens 8*th .. 8*th+7 with th = (o % 32) / 16
-      const int d = o >> 5, th = (o & 31) >> 4;
+    {  // V: words 0-1 = dimension 32c + li, words 2-3 = dimension 32c + 16 + li
       u32x4 val = r.valid ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
       if (boundary) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int ta = tok_base + 8 * th + 2 * e;
+          const int ta = tok_base + 4 * g + 2 * (e & 1);
           uint32_t keep = 0u;
           if (ta >= p.kv_begin && ta < p.kv_end) keep |= 0x0000ffffu;
           if (ta + 1 >= p.kv_begin && ta + 1 < p.kv_end) keep |= 0xffff0000u;
@@ -147,10 +151,11 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& r, cons
         val[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
                                                   __uint_as_float(val[e] << 16),
                                                   __uint_as_float(val[e] & 0xffff0000u)));
-      // tokens 8th+0..3 -> half 0, tokens 8th+4..7 -> half 1; byte offset 8*th
-      const u32x2 lo = {val[0], val[1]}, hi = {val[2], val[3]};
-      *reinterpret_cast<u32x2*>(vs + v_lds_off(pg, d, 0) + 8 * th) = lo;
-      *reinterpret_cast<u32x2*>(vs + v_lds_off(pg, d, 1) + 8 * th) = hi;
+      // tokens 4g .. 4g+3 go to half g & 1 at byte 8 * (g >> 1)
+      const int d0 = 32 * c + li;
+      const u32x2 a = {val[0], val[1]}, b = {val[2], val[3]};
+      *reinterpret_cast<u32x2*>(vs + v_lds_off(pg, d0, g & 1) + 8 * (g >> 1)) = a;
+      *reinterpret_cast<u32x2*>(vs + v_lds_off(pg, d0 + 16, g & 1) + 8 * (g >> 1)) = b;
     }
   }
 }

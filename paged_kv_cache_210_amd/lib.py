@@ -131,8 +131,9 @@ def _need(t, dtype, name, device=None, shape=None):
 # ---------------------------------------------------------------- cache
 class PagedCache:
     """One layer's block pool: K [num_blocks, Hkv, 16, d], V [num_blocks, Hkv, d, 16]
-    (E4M3 pools are uint8 with fp32 scales [num_blocks, Hkv]; their pages hold
-    the same bytes in the fragment order pkv.h documents)."""
+    tensors (E4M3 pools are uint8 with fp32 scales [num_blocks, Hkv]).  f32
+    pages use those shapes' natural order; bf16 and E4M3 pages hold the same
+    elements in the fragment order pkv.h documents."""
 
     def __init__(self, k, v, kv_dtype: int, k_scale=None, v_scale=None):
         self.k, self.v = k, v

@@ -36,16 +36,21 @@ def kv_elements(t, fmt):
     return t.detach().cpu().numpy()
 
 
-def e4m3_pages_logical(k_phys, v_phys):
-    """E4M3 pool bytes in the fragment order include/pkv.h documents -> logical
-    code arrays K [..., 16, d] and V [..., d, 16] (the oracle's layout)."""
+def frag_pages_logical(k_phys, v_phys, es):
+    """Pool pages in the fragment order include/pkv.h documents (bf16: es 2,
+    E4M3: es 1; arrays of elements [nb, hkv, 16*d] in any shape) -> logical
+    K [nb, hkv, 16, d] and V [nb, hkv, d, 16] (the oracle's layout)."""
     k_phys, v_phys = np.asarray(k_phys), np.asarray(v_phys)
-    nb, hkv, _, D = k_phys.shape
+    nb, hkv = k_phys.shape[:2]
+    D = k_phys[0, 0].size // 16
     t = np.arange(16)[:, None]
     d = np.arange(D)[None, :]
-    c, grp, nn = d >> 5, (d >> 3) & 3, d >> 4
-    koff = (c >> 1) * 1024 + ((grp << 4) + t) * 16 + (c & 1) * 8 + (d & 7)              # [t, d]
-    voff = (nn >> 2) * 1024 + (((t >> 2) << 4) + (d & 15)) * 16 + (nn & 3) * 4 + (t & 3)  # [t, d]
+    c, g, n = d >> 5, (d >> 3) & 3, d >> 4
+    cpp, npp = 2 // es, 4 // es
+    koff = (c // cpp) * 1024 + ((g << 4) + t) * 16 + (c % cpp) * 8 * es + (d & 7) * es
+    voff = (n // npp) * 1024 + (((t >> 2) << 4) + (d & 15)) * 16 + (n % npp) * 4 * es + (t & 3) * es
+    assert np.all(koff % es == 0) and np.all(voff % es == 0)
+    koff, voff = koff // es, voff // es                     # element offsets, [t, d]
     assert len(np.unique(koff)) == 16 * D and len(np.unique(voff)) == 16 * D
     kf = k_phys.reshape(nb, hkv, 16 * D)
     vf = v_phys.reshape(nb, hkv, 16 * D)

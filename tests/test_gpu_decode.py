@@ -9,7 +9,7 @@ import torch
 
 from oracle import pkv_oracle as O
 import synth
-from tests._util import (TOL, bits, compare_rows, e4m3_pages_logical, gpu_cache, kv_elements,
+from tests._util import (TOL, bits, compare_rows, frag_pages_logical, gpu_cache, kv_elements,
                          oracle_cache, q_elements)
 
 pytestmark = pytest.mark.gpu
@@ -60,9 +60,9 @@ def _pool_equal(cache, oc, blocks=None):
     gk = cache.k.cpu()
     gv = cache.v.cpu()
     if oc.fmt == "bf16":
-        gk, gv = bits(gk), bits(gv)
+        gk, gv = frag_pages_logical(bits(gk), bits(gv), 2)
     elif oc.fmt == "e4m3":
-        gk, gv = e4m3_pages_logical(gk.numpy(), gv.numpy())
+        gk, gv = frag_pages_logical(gk.numpy(), gv.numpy(), 1)
     else:
         gk, gv = gk.numpy(), gv.numpy()
     if blocks is not None:
