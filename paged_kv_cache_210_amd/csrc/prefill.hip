@@ -88,14 +88,23 @@ struct TileRegs {
   bool valid;
 };
 
-__device__ __forceinline__ void load_tile(TileRegs& r, const PrefillParams& p, int tile, int tid,
-                                          int kvh) {
-  const int pg = tid >> 7, t128 = tid & 127;
-  const int lblk = tile * 4 + pg;
-  int blk = -1;
-  if (lblk < p.maxb && lblk * kBlock < p.kv_end) blk = p.table[lblk];
-  r.valid = (unsigned)blk < (unsigned)p.num_blocks;
-  if (!r.valid) return;
+// Table entry of this thread's page (tid / 128) of a tile, read at a clamped
+// index (always in bounds; whether the page exists is decided by load_tile).
+// Read one step before the page loads that need it, and never under a
+// branch, so the page loads never wait on the table.
+__device__ __forceinline__ int tile_entry(const PrefillParams& p, int tile, int tid) {
+  return p.table[min(tile * 4 + (tid >> 7), p.maxb - 1)];
+}
+
+// Page loads of a tile.  A page past kv_end or the table, or whose entry is
+// outside the pool, is marked invalid (stored as zeros); its loads still run,
+// from block 0, so that no load sits under a branch.
+__device__ __forceinline__ void load_tile(TileRegs& r, const PrefillParams& p, int tile, int entry,
+                                          int tid, int kvh) {
+  const int t128 = tid & 127;
+  const int lblk = tile * 4 + (tid >> 7);
+  r.valid = lblk < p.maxb && lblk * kBlock < p.kv_end && (unsigned)entry < (unsigned)p.num_blocks;
+  const int blk = r.valid ? entry : 0;
   const uint8_t* kp = p.k + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * kBlock * D * 2;
   const uint8_t* vp = p.v + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * D * kBlock * 2;
 #pragma unroll
@@ -339,12 +348,13 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
 
   if (t_lo <= t_hi) {
     TileRegs regs;
-    load_tile(regs, p, t_lo, tid, kvh);
+    load_tile(regs, p, t_lo, tile_entry(p, t_lo, tid), tid, kvh);
     store_tile(smem, regs, p, t_lo, tid);
     if (t_lo + 1 <= t_hi) {
-      load_tile(regs, p, t_lo + 1, tid, kvh);
+      load_tile(regs, p, t_lo + 1, tile_entry(p, t_lo + 1, tid), tid, kvh);
       store_tile(smem + BUF_BYTES, regs, p, t_lo + 1, tid);
     }
+    int entry_next = tile_entry(p, t_lo + 2, tid);
     __syncthreads();
 
     f32x16 sa[2], sb[2];
@@ -362,7 +372,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
       const int s2 = s1 == 2 ? 0 : s1 + 1;
       const bool prefetch = j + 2 <= t_hi;
       TileRegs nregs;
-      if (prefetch) load_tile(nregs, p, j + 2, tid, kvh);
+      if (prefetch) load_tile(nregs, p, j + 2, entry_next, tid, kvh);
+      entry_next = tile_entry(p, j + 3, tid);
       attend_step<NEG_SCALE>(st, s_cur, s_next, smem + slot * BUF_BYTES, smem + s1 * BUF_BYTES,
                              qf, c, qr, hi);
       if (prefetch) store_tile(smem + s2 * BUF_BYTES, nregs, p, j + 2, tid);
