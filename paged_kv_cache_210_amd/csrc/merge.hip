@@ -15,14 +15,20 @@ namespace {
 
 constexpr int kMaxD = 256;
 
-// Many parts (long decode splits): one workgroup per row.  The max and the
-// sum of weights are reduced over all threads; for O~ the workgroup is split
-// into groups of D/VEC threads, each group walking every NG-th part with
-// VEC-wide loads, and the groups are summed in LDS.
+// Many parts (long decode splits): one workgroup of 512 threads per row.
+// The part weights a_s = exp(m_s - M) (0 for parts with no visible key) go to
+// LDS once; then groups of D/VEC threads walk every NG-th part with VEC-wide
+// loads of O~, and the groups are summed in LDS.  Parts are taken in chunks
+// of kChunk so any S fits.
+constexpr int kMergeThreads = 512;
+constexpr int kChunk = 2048;
+
 template <int VEC>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  __shared__ float red[2][4];
-  __shared__ float osum[256 * VEC];
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  constexpr int NW = kMergeThreads / 64;
+  __shared__ float red[NW];
+  __shared__ float wts[kChunk];
+  __shared__ float osum[kMergeThreads * VEC];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = tid >> 6;
@@ -31,55 +37,66 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const float f = kLog2e;               // m in natural units
 
   float mx = -INFINITY;
-  for (int s = tid; s < a.S; s += 256) {
+  for (int s = tid; s < a.S; s += kMergeThreads) {
     const float ms = mrow[s * a.ml_part], ls = lrow[s * a.ml_part];
     if (ls > 0.f && ms > -INFINITY) mx = fmaxf(mx, ms);
   }
   mx = wave_max(mx);
-  if (lane == 0) red[0][w] = mx;
+  if (lane == 0) red[w] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-
-  float L = 0.f;
-  if (M > -INFINITY) {
-    for (int s = tid; s < a.S; s += 256) {
-      const float ms = mrow[s * a.ml_part], ls = lrow[s * a.ml_part];
-      if (ls > 0.f && ms > -INFINITY) L += __builtin_amdgcn_exp2f((ms - M) * f) * ls;
-    }
-  }
-  L = wave_sum(L);
-  if (lane == 0) red[1][w] = L;
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
+  __syncthreads();                      // red is reused for L below
+  const bool any = M > -INFINITY;
 
   const int lanes = (a.D + VEC - 1) / VEC;          // threads per group
-  const int ng = 256 / lanes;                        // groups
+  const int ng = kMergeThreads / lanes;              // groups
   const int gi = tid / lanes, li = tid - gi * lanes;
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  if (M > -INFINITY && gi < ng && li * VEC < a.D) {
-    const float* orow = a.o + row * a.o_row + li * VEC;
-#pragma unroll 4
-    for (int s = gi; s < a.S; s += ng) {
+  float L = 0.f;
+  const float* orow = a.o + row * a.o_row + li * VEC;
+  for (int s0 = 0; s0 < a.S; s0 += kChunk) {
+    const int n = min(kChunk, a.S - s0);
+    for (int i = tid; i < n; i += kMergeThreads) {
+      const int s = s0 + i;
       const float ms = mrow[s * a.ml_part], ls = lrow[s * a.ml_part];
-      if (ls > 0.f && ms > -INFINITY) {
-        const float ws = __builtin_amdgcn_exp2f((ms - M) * f);
-        const float* op = orow + s * a.o_part;
-        if constexpr (VEC == 4) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(op);
+      const bool live = any && ls > 0.f && ms > -INFINITY;
+      const float ws = live ? __builtin_amdgcn_exp2f((ms - M) * f) : 0.f;
+      wts[i] = ws;
+      if (live) L += ws * ls;
+    }
+    __syncthreads();
+    if (gi < ng && li * VEC < a.D) {
+#pragma unroll 4
+      for (int i = gi; i < n; i += ng) {
+        const float ws = wts[i];
+        if (ws != 0.f) {                // parts with no visible key are skipped
+          const float* op = orow + (int64_t)(s0 + i) * a.o_part;
+          if constexpr (VEC == 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(op);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] += ws * v[e];
-        } else {
-          acc[0] += ws * op[0];
+            for (int e = 0; e < 4; ++e) acc[e] += ws * v[e];
+          } else {
+            acc[0] += ws * op[0];
+          }
         }
       }
     }
+    __syncthreads();                    // wts is rewritten by the next chunk
   }
+  L = wave_sum(L);
+  if (lane == 0) red[w] = L;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) osum[tid * VEC + e] = acc[e];
   __syncthreads();
-  const float Lt = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-  const bool empty = !(M > -INFINITY) || !(Lt > 0.f);
-  for (int d = tid; d < a.D; d += 256) {
+  float Lt = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) Lt += red[i];
+  const bool empty = !any || !(Lt > 0.f);
+  for (int d = tid; d < a.D; d += kMergeThreads) {
     float o = 0.f;
     const int l0 = d / VEC, e = d - l0 * VEC;
     for (int g = 0; g < ng; ++g) o += osum[(g * lanes + l0) * VEC + e];
@@ -97,15 +114,21 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
 }
 
-// Few parts (prefill shards, short decode splits): one wave per row, four
-// rows per workgroup, lanes over the dims; every part's m and l are read with
-// scalar loads and all of a row's O~ loads are issued back to back.
+// Few parts (prefill shards, short decode splits).  Rows are spread over the
+// lanes of a wave, D/4 lanes per row, each lane owning 4 consecutive
+// dimensions (16-byte loads); every part's m and l are read per lane (lanes
+// of a row read the same address).  Needs D % 4 == 0, D <= 256 and 16-byte
+// aligned part rows.
 constexpr int kFewParts = 16;
 
 __global__ __launch_bounds__(256) void merge_rows_kernel(MergeArgs a) {
+  const int lanes = a.D >> 2;                            // lanes per row
+  const int rpw = 64 / lanes;                            // rows per wave (>= 1)
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= a.rows) return;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int li = lane % lanes;
+  const int64_t row = (int64_t)wave * rpw + lane / lanes;
+  if (lane >= rpw * lanes || row >= a.rows) return;
   const float* mrow = a.m + row * a.ml_row;
   const float* lrow = a.l + row * a.ml_row;
   const float f = kLog2e;               // m in natural units
@@ -120,37 +143,28 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(MergeArgs a) {
     }
   }
   const bool any = M > -INFINITY;
-  constexpr int kPer = kMaxD / 64;
-  float acc[kPer];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  const float* orow = a.o + row * a.o_row;
+  const float* orow = a.o + row * a.o_row + 4 * li;
 #pragma unroll
   for (int s = 0; s < kFewParts; ++s) {
     if (s < a.S && any && ls[s] > 0.f && ms[s] > -INFINITY) {
       const float ws = __builtin_amdgcn_exp2f((ms[s] - M) * f);
       L += ws * ls[s];
-      const float* op = orow + s * a.o_part;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        const int d = lane + 64 * e;
-        if (d < a.D) acc[e] += ws * op[d];
-      }
+      acc += ws * *reinterpret_cast<const f32x4*>(orow + s * a.o_part);
     }
   }
   const bool empty = !any || !(L > 0.f);
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int d = lane + 64 * e;
-    if (d >= a.D) continue;
-    const float o = empty ? 0.f : acc[e] / L;
-    if (a.out_dtype == PKV_BF16)
-      reinterpret_cast<uint16_t*>(a.out)[row * a.D + d] = f32_to_bf16_bits(o);
-    else
-      reinterpret_cast<float*>(a.out)[row * a.D + d] = o;
+  const f32x4 o = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : acc / L;
+  if (a.out_dtype == PKV_BF16) {
+    u32x2 pk;
+    pk.x = (uint32_t)f32_to_bf16_bits(o.x) | ((uint32_t)f32_to_bf16_bits(o.y) << 16);
+    pk.y = (uint32_t)f32_to_bf16_bits(o.z) | ((uint32_t)f32_to_bf16_bits(o.w) << 16);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + row * a.D + 4 * li) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + row * a.D + 4 * li) = o;
   }
-  if (lane == 0) {
+  if (li == 0) {
     const float Mn = empty ? -INFINITY : M;
     if (a.out_m) a.out_m[row] = Mn;
     if (a.out_l) a.out_l[row] = empty ? 0.f : L;
@@ -163,17 +177,19 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(MergeArgs a) {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (a.D > kMaxD || a.rows > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.S <= kFewParts) {
-    const int64_t wgs = (a.rows + 3) / 4;
-    hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a);
+  // 16-byte loads of O~ need 16-byte aligned part rows (and 4 | D); the
+  // output rows then are 8-byte (bf16) or 16-byte (fp32) aligned as well
+  const bool vec4 = (a.D % 4) == 0 && (a.o_row % 4) == 0 && (a.o_part % 4) == 0 &&
+                    (reinterpret_cast<uintptr_t>(a.o) & 15u) == 0 &&
+                    (reinterpret_cast<uintptr_t>(a.out) & (a.out_dtype == PKV_BF16 ? 7u : 15u)) == 0;
+  if (a.S <= kFewParts && vec4 && 64 % (a.D / 4) == 0) {
+    const int rpw = 64 / (a.D / 4);
+    const int64_t waves = (a.rows + rpw - 1) / rpw;
+    hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+  } else if (vec4) {
+    hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)a.rows), dim3(kMergeThreads), 0, s, a);
   } else {
-    // VEC-wide loads need 16-byte aligned part rows
-    const bool vec4 = (a.D % 4) == 0 && (a.o_row % 4) == 0 && (a.o_part % 4) == 0 &&
-                      (reinterpret_cast<uintptr_t>(a.o) & 15u) == 0;
-    if (vec4)
-      hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)a.rows), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)a.rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)a.rows), dim3(kMergeThreads), 0, s, a);
   }
   return hipGetLastError();
 }
