@@ -113,7 +113,9 @@ def bench_decode(cfg, steps, warmup, partition_blocks=0):
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / steps
-    ms_dec = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    dec = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    st["decode_ms_median"], st["decode_ms_min"] = dec[len(dec) // 2], dec[0]
+    ms_dec = sum(dec) / steps
     ms_merge = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     return ms_step, ms_dec, ms_merge, st
 
@@ -137,7 +139,8 @@ def decode_record(cfg, steps, warmup, partition_blocks):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / A.HBM_PEAK_GBS, "traffic": measured_traffic(cfg),
                      "kernel": "decode_mfma_kernel (pkv_paged_attn_decode_partial)",
-                     "ms_per_launch": ms_dec, "bytes_per_launch": kbytes},
+                     "ms_per_launch": ms_dec, "ms_per_launch_median": st["decode_ms_median"],
+                     "ms_per_launch_min": st["decode_ms_min"], "bytes_per_launch": kbytes},
     }
     return rec, st
 
@@ -320,6 +323,48 @@ def cpu_baseline_decode(cfg, budget_s):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def cpu_baseline_prefill(cfg, budget_s, device="cuda"):
+    """The fp64 oracle, as it stands, on a bounded sample of the same causal
+    prefill: query rows taken from the end of the prompt (the longest ones),
+    each against all of its visible keys, all heads.  The rate is attention
+    flops (4*d per visible key per head) per second, the same unit as the GPU
+    figure; the prompt's KV is put into the oracle pool untimed."""
+    import numpy as np
+    import torch
+    from oracle import pkv_oracle as O
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas_threads = 1
+    inp = synth.prefill_inputs(cfg, device=device)
+    tables, _ = O.build_tables([cfg.prompt_len], cfg.pool_blocks, inp["free_order"].numpy())
+
+    def bits(t):
+        return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    cache = O.new_cache(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16")
+    O.append_sequence(cache, bits(inp["k"]), bits(inp["v"]), tables[0], 0)   # untimed
+    q = bits(inp["q"])
+    rows, pairs, spent = 0, 0, 0.0
+    for r in range(cfg.prompt_len - 1, -1, -1):
+        t0 = time.perf_counter()
+        O.prefill(cache, q[r:r + 1], "bf16", r, tables[0], 0, r + 1, True)
+        spent += time.perf_counter() - t0
+        rows += 1
+        pairs += r + 1
+        if spent >= budget_s:
+            break
+    flops = 4 * cfg.head_dim * cfg.hq * pairs
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{rows} query rows (the last ones) of {cfg.name}, each against all its "
+                      f"visible keys, all {cfg.hq} heads, {spent:.1f} s of CPU time",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -379,6 +424,8 @@ def main(argv=None):
             c = synth.CONFIGS[name]
             _log(f"[bench] secondary {c.name}")
             rec = prefill_record(c, args.prefill_reps)
+            if name == "C4" and not args.no_cpu_baseline:
+                rec["cpu_baseline"] = cpu_baseline_prefill(c, args.cpu_seconds / 2)
             secondary.append(rec)
             _log(f"[bench]   {rec['tflops']:.0f} TFLOP/s, {rec['ms_per_prompt']:.2f} ms/prompt")
 
