@@ -133,11 +133,16 @@ def test_prefill_row_equals_decode(lib):
         assert diff <= 8e-3, (p, diff)       # two bf16 roundings of the same value
 
 
-def test_chunked_prefill_c4_sampled(lib):
-    """The 32768-token prompt in 4096-token chunks, KV in 4 sequential 8192-token
-    shards merged by LSE, as the whole-prompt flow runs it; sampled rows are
-    checked against the oracle."""
-    cfg = synth.CONFIGS["C4"]
+@pytest.mark.parametrize("name,rows", [
+    ("C4", [0, 1, 4095, 4096, 8191, 8192, 16000, 24575, 30001, 32767]),
+    ("C4_128K", [0, 32767, 32768, 65537, 98303, 131071]),
+])
+def test_chunked_prefill_sampled(lib, name, rows):
+    """The whole prompt in 4096-token chunks, KV in sequential shards merged by
+    LSE, as bench.py runs it (C4: 32768 tokens, 8192-token shards; C4-128K:
+    131072 tokens, 32768-token shards); sampled rows, including each shard's
+    first and last, are checked against the oracle."""
+    cfg = synth.CONFIGS[name]
     inp = synth.prefill_inputs(cfg, device=DEV)
     tables, _ = lib.build_tables([cfg.prompt_len], cfg.pool_blocks, inp["free_order"])
     td = tables.to(DEV)
@@ -156,7 +161,7 @@ def test_chunked_prefill_c4_sampled(lib):
         lib.attn_lse_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]),
                            torch.stack([p[2] for p in parts]), out=outs[a:b], with_state=False)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 4095, 4096, 8191, 8192, 16000, 24575, 30001, 32767])
+    rows = np.array(rows)
     tab = tables.numpy()
     dcfg = synth.decode_config("o", (cfg.prompt_len,), cfg.hq, cfg.hkv, 128,
                                pool_blocks=cfg.pool_blocks)
@@ -165,4 +170,4 @@ def test_chunked_prefill_c4_sampled(lib):
     got = outs[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
     for i, r in enumerate(rows):
         ref = O.prefill(oc, qs[i:i + 1], "bf16", int(r), tab[0], 0, int(r) + 1, True)
-        compare_rows(got[i:i + 1], ref["o"], "bf16", f"C4 row {r}")
+        compare_rows(got[i:i + 1], ref["o"], "bf16", f"{name} row {r}")
