@@ -226,7 +226,8 @@ int32_t pkv_paged_attn_decode_partial(const pkv_cache_desc* cache, const void* q
  * Query rows q[r] (r < T) of one sequence sit at absolute positions q_pos0+r.
  * Row r attends to keys t with kv_begin <= t < kv_end and, when causal, t <=
  * q_pos0 + r, read through block_table (device int32 [max_blocks], covering
- * kv_end).  q: device [T][num_q_heads][head_dim] bf16; head_dim 128.
+ * kv_end).  q: device [T][num_q_heads][head_dim] bf16; a bf16 cache with
+ * head_dim 64 or 128 (otherwise PKV_ERR_UNSUPPORTED).
  * Exactly one output form:
  *  - final:   out (device bf16 [T][num_q_heads][head_dim]) = normalised O,
  *             out_lse (nullable, fp32 [T][num_q_heads]);

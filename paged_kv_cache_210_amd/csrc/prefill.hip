@@ -35,15 +35,24 @@
 namespace pkv {
 namespace {
 
-constexpr int D = 128;
 constexpr int BN = 64;                   // tokens per K/V tile (4 pages)
 constexpr int ROWS_W = 32;               // query rows per wave
 constexpr int NWAVE = 8;
 constexpr int NTHREADS = 64 * NWAVE;
-constexpr int TILE_BYTES = BN * D * 2;   // 16 KiB for K, same for V
-constexpr int BUF_BYTES = 2 * TILE_BYTES;
 constexpr int NBUF = 3;                  // LDS ring of K/V tiles
-constexpr int LDS_BYTES = NBUF * BUF_BYTES;
+
+// Sizes for head dimension D (64 or 128).
+template <int D>
+struct Geo {
+  static constexpr int TILE = BN * D * 2;        // bytes of a K (or V) tile: 16 KiB at D 128
+  static constexpr int BUF = 2 * TILE;           // one ring slot: K tile + V tile
+  static constexpr int LDS = NBUF * BUF;
+  static constexpr int PAGE = kBlock * D * 2;    // bytes of one page
+  static constexpr int SPT = PAGE / 2048;        // 16-byte pieces per staging thread (128 per page)
+  static constexpr int NCH = D / 8;              // 16-byte chunks per key
+  static constexpr int QC = D / 16;              // k-steps of the score product
+  static constexpr int DT = D / 32;              // 32-dimension blocks of O
+};
 constexpr float kLazy = 8.0f;            // log2 headroom of the running max
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -69,22 +78,29 @@ struct PrefillParams {
   float* part_l;
 };
 
-// LDS K tile: [64 tokens][16 chunks of 16 B]; chunk c of token t sits at
-// c ^ (t & 15) so 16 lanes reading one chunk column hit 16 distinct chunks.
-__device__ __forceinline__ int k_lds_off(int t, int c) { return t * 256 + ((c ^ (t & 15)) << 4); }
+// LDS K tile: [64 tokens][D/8 chunks of 16 B]; chunk c of token t sits at
+// c ^ f(t), f(t) = (t % 16) / (16 / (D/8)), so the 16 lanes that read one chunk
+// of 16 consecutive tokens hit 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_lds_off(int t, int c) {
+  constexpr int NCH = Geo<D>::NCH;
+  return t * (D * 2) + ((c ^ ((t & 15) / (16 / NCH))) << 4);
+}
 
 // LDS V tile: [4 pages][128 dims][32 B]; within a dimension the 16 tokens are
 // stored as halves {0-3, 8-11} and {4-7, 12-15} (the token sets one 32x32x16
 // k-step takes from each lane half), and the halves swap when (d >> 3) is odd.
+template <int D>
 __device__ __forceinline__ int v_lds_off(int page, int d, int half) {
-  return page * 4096 + d * 32 + ((half ^ ((d >> 3) & 1)) << 4);
+  return page * (D * 32) + d * 32 + ((half ^ ((d >> 3) & 1)) << 4);
 }
 
 // Staging: thread tid moves page tid / 128 of the tile, bytes
-// [i*2048 + (tid % 128)*16, +16) of that page's K and of its V (i = 0, 1).
+// [i*2048 + (tid % 128)*16, +16) of that page's K and of its V (i < SPT).
+template <int D>
 struct TileRegs {
-  u32x4 k[2];
-  u32x4 v[2];
+  u32x4 k[Geo<D>::SPT];
+  u32x4 v[Geo<D>::SPT];
   bool valid;
 };
 
@@ -99,8 +115,9 @@ __device__ __forceinline__ int tile_entry(const PrefillParams& p, int tile, int 
 // Page loads of a tile.  A page past kv_end or the table, or whose entry is
 // outside the pool, is marked invalid (stored as zeros); its loads still run,
 // from block 0, so that no load sits under a branch.
-__device__ __forceinline__ void load_tile(TileRegs& r, const PrefillParams& p, int tile, int entry,
-                                          int tid, int kvh) {
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillParams& p, int tile,
+                                          int entry, int tid, int kvh) {
   const int t128 = tid & 127;
   const int lblk = tile * 4 + (tid >> 7);
   r.valid = lblk < p.maxb && lblk * kBlock < p.kv_end && (unsigned)entry < (unsigned)p.num_blocks;
@@ -108,7 +125,7 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const PrefillParams& p, i
   const uint8_t* kp = p.k + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * kBlock * D * 2;
   const uint8_t* vp = p.v + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * D * kBlock * 2;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < Geo<D>::SPT; ++i) {
     r.k[i] = *reinterpret_cast<const u32x4*>(kp + i * 2048 + t128 * 16);
     r.v[i] = *reinterpret_cast<const u32x4*>(vp + i * 2048 + t128 * 16);
   }
@@ -122,15 +139,16 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const PrefillParams& p, i
 // Tokens outside [kv_begin, kv_end) get zero K and V on boundary tiles, and
 // pages without a valid block are all zero, so masked positions contribute
 // exactly nothing to P V.
-__device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& r, const PrefillParams& p,
-                                           int tile, int tid) {
+template <int D>
+__device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs<D>& r,
+                                           const PrefillParams& p, int tile, int tid) {
   uint8_t* ks = buf;
-  uint8_t* vs = buf + TILE_BYTES;
+  uint8_t* vs = buf + Geo<D>::TILE;
   const int pg = tid >> 7, t128 = tid & 127;
   const int tok_base = tile * BN + pg * kBlock;   // first token of this page
   const bool boundary = tile * BN < p.kv_begin || tile * BN + BN > p.kv_end;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < Geo<D>::SPT; ++i) {
     const int o = i * 2048 + t128 * 16;
     const int c = o >> 10, l = (o >> 4) & 63, g = l >> 4, li = l & 15;
     {  // K: token li, chunk 4c + g
@@ -139,7 +157,7 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& r, cons
         const int ta = tok_base + li;
         if (ta < p.kv_begin || ta >= p.kv_end) val = u32x4{0u, 0u, 0u, 0u};
       }
-      *reinterpret_cast<u32x4*>(ks + k_lds_off(pg * kBlock + li, 4 * c + g)) = val;
+      *reinterpret_cast<u32x4*>(ks + k_lds_off<D>(pg * kBlock + li, 4 * c + g)) = val;
     }
     {  // V: words 0-1 = dimension 32c + li, words 2-3 = dimension 32c + 16 + li
       u32x4 val = r.valid ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
@@ -163,30 +181,32 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& r, cons
       // tokens 4g .. 4g+3 go to half g & 1 at byte 8 * (g >> 1)
       const int d0 = 32 * c + li;
       const u32x2 a = {val[0], val[1]}, b = {val[2], val[3]};
-      *reinterpret_cast<u32x2*>(vs + v_lds_off(pg, d0, g & 1) + 8 * (g >> 1)) = a;
-      *reinterpret_cast<u32x2*>(vs + v_lds_off(pg, d0 + 16, g & 1) + 8 * (g >> 1)) = b;
+      *reinterpret_cast<u32x2*>(vs + v_lds_off<D>(pg, d0, g & 1) + 8 * (g >> 1)) = a;
+      *reinterpret_cast<u32x2*>(vs + v_lds_off<D>(pg, d0 + 16, g & 1) + 8 * (g >> 1)) = b;
     }
   }
 }
 
+template <int D>
 struct RowState {
-  f32x16 o[4];     // O^T[32*dt + 8*(r/4) + 4*(lane/32) + r%4][row]
+  f32x16 o[Geo<D>::DT];   // O^T[32*dt + 8*(r/4) + 4*(lane/32) + r%4][row]
   float m, l;      // running max (log2 units, lazy) and this lane's share of the sum
   float mtrue;     // this lane's exact max of the scaled scores
 };
 
 // S^T for one tile: s[mt][r] = score of key 32*mt + 8*(r/4) + 4*hi + r%4.
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const uint8_t* ks, const u32x4 (&qf)[8],
-                                        int qr, int hi) {
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const uint8_t* ks,
+                                        const u32x4 (&qf)[Geo<D>::QC], int qr, int hi) {
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+  for (int c = 0; c < Geo<D>::QC; ++c)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + k_lds_off(32 * mt + qr, 2 * c + hi));
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + k_lds_off<D>(32 * mt + qr, 2 * c + hi));
       s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
                                                      __builtin_bit_cast(bf16x8, qf[c]), s[mt], 0,
                                                      0, 0);
@@ -221,8 +241,8 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const PrefillParams& p
 // The max is raised only when a score exceeds it by more than kLazy, which
 // keeps every weight below 2^kLazy; then the row's lane pair agrees on the new
 // max and O, l are rescaled.  Returns the max to subtract.
-template <bool NEG_SCALE>
-__device__ __forceinline__ float update_max(RowState& st, const f32x16 (&s)[2], float c) {
+template <int D, bool NEG_SCALE>
+__device__ __forceinline__ float update_max(RowState<D>& st, const f32x16 (&s)[2], float c) {
   const float hidden = NEG_SCALE ? INFINITY : -INFINITY;
   float ext = hidden;
 #pragma unroll
@@ -239,7 +259,7 @@ __device__ __forceinline__ float update_max(RowState& st, const f32x16 (&s)[2], 
     const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m - m_new);
     st.l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
+    for (int dt = 0; dt < Geo<D>::DT; ++dt) st.o[dt] *= alpha;
     st.m = m_new;
   }
   return st.m == -INFINITY ? 0.f : st.m;
@@ -250,12 +270,14 @@ __device__ __forceinline__ float update_max(RowState& st, const f32x16 (&s)[2], 
 // run into s_next, then O^T += V^T P^T for tile j.  The row sum is taken over
 // the rounded weights that enter the product, so the result stays an exact
 // weighted average of V rows.
-template <bool NEG_SCALE>
-__device__ __forceinline__ void attend_step(RowState& st, const f32x16 (&s_cur)[2],
+template <int D, bool NEG_SCALE>
+__device__ __forceinline__ void attend_step(RowState<D>& st, const f32x16 (&s_cur)[2],
                                             f32x16 (&s_next)[2], const uint8_t* cur,
-                                            const uint8_t* nxt, const u32x4 (&qf)[8], float c,
-                                            int qr, int hi) {
-  const float m_use = update_max<NEG_SCALE>(st, s_cur, c);
+                                            const uint8_t* nxt, const u32x4 (&qf)[Geo<D>::QC],
+                                            float c, int qr, int hi) {
+  constexpr int QC = Geo<D>::QC;
+  constexpr int WPC = 32 / QC;          // weights made per k-step of the score product
+  const float m_use = update_max<D, NEG_SCALE>(st, s_cur, c);
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -264,39 +286,41 @@ __device__ __forceinline__ void attend_step(RowState& st, const f32x16 (&s_cur)[
   f16x8 pb[4];      // k-step ks = 2*mt + rr takes s_cur[mt][8*rr .. 8*rr+7]
   float rs = 0.f;
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
+  for (int cc = 0; cc < QC; ++cc) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const u32x4 kf = *reinterpret_cast<const u32x4*>(nxt + k_lds_off(32 * mt + qr, 2 * cc + hi));
+      const u32x4 kf =
+          *reinterpret_cast<const u32x4*>(nxt + k_lds_off<D>(32 * mt + qr, 2 * cc + hi));
       s_next[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
                                                           __builtin_bit_cast(bf16x8, qf[cc]),
                                                           s_next[mt], 0, 0, 0);
     }
-    const int kst = cc >> 1, e0 = (cc & 1) * 4;
+    const int kst = (cc * WPC) >> 3, e0 = (cc * WPC) & 7;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < WPC; ++e)
       pb[kst][e0 + e] = (_Float16)__builtin_amdgcn_exp2f(
           __builtin_fmaf(s_cur[kst >> 1][8 * (kst & 1) + e0 + e], c, -m_use));
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < WPC / 2; ++e) {
       const f16x2 pr = {pb[kst][e0 + 2 * e], pb[kst][e0 + 2 * e + 1]};
       rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
     }
   }
   st.l += rs;
-  const uint8_t* vs = cur + TILE_BYTES;
+  const uint8_t* vs = cur + Geo<D>::TILE;
 #pragma unroll
   for (int kst = 0; kst < 4; ++kst)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + v_lds_off(kst, 32 * dt + qr, hi));
+    for (int dt = 0; dt < Geo<D>::DT; ++dt) {
+      const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + v_lds_off<D>(kst, 32 * dt + qr, hi));
       st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf), pb[kst],
                                                        st.o[dt], 0, 0, 0);
     }
 }
 
-template <bool NEG_SCALE>
+template <int D, bool NEG_SCALE>
 __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
+  using G = Geo<D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -319,11 +343,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
   const int my_pos = p.q_pos0 + my_row;
 
   // query fragments (B operand): Q[row][16c + 8*hi .. +8]
-  u32x4 qf[8];
+  u32x4 qf[G::QC];
   {
     const uint16_t* qp = p.q + ((int64_t)my_row * p.hq + h) * D;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < G::QC; ++c)
       qf[c] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * c + 8 * hi)
                      : u32x4{0u, 0u, 0u, 0u};
   }
@@ -336,9 +360,9 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
   const int t_hi = key_end > p.kv_begin ? (key_end - 1) / BN : t_lo - 1;
   const int w_minpos = p.q_pos0 + wrow0;
 
-  RowState st;
+  RowState<D> st;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.o[dt][r] = 0.f;
   st.m = -INFINITY;
@@ -347,18 +371,18 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
   const float c = p.scale_log2;
 
   if (t_lo <= t_hi) {
-    TileRegs regs;
+    TileRegs<D> regs;
     load_tile(regs, p, t_lo, tile_entry(p, t_lo, tid), tid, kvh);
     store_tile(smem, regs, p, t_lo, tid);
     if (t_lo + 1 <= t_hi) {
       load_tile(regs, p, t_lo + 1, tile_entry(p, t_lo + 1, tid), tid, kvh);
-      store_tile(smem + BUF_BYTES, regs, p, t_lo + 1, tid);
+      store_tile(smem + G::BUF, regs, p, t_lo + 1, tid);
     }
     int entry_next = tile_entry(p, t_lo + 2, tid);
     __syncthreads();
 
     f32x16 sa[2], sb[2];
-    qk_tile(sa, smem, qf, qr, hi);
+    qk_tile<D>(sa, smem, qf, qr, hi);
     if (tile_needs_mask(p, t_lo * BN, w_minpos)) mask_tile<NEG_SCALE>(sa, p, t_lo * BN, my_pos, hi);
 
     // Tile j lives in ring slot (j - t_lo) % 3.  Step j loads tile j+2 into
@@ -371,12 +395,12 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
       const int s1 = slot == 2 ? 0 : slot + 1;
       const int s2 = s1 == 2 ? 0 : s1 + 1;
       const bool prefetch = j + 2 <= t_hi;
-      TileRegs nregs;
+      TileRegs<D> nregs;
       if (prefetch) load_tile(nregs, p, j + 2, entry_next, tid, kvh);
       entry_next = tile_entry(p, j + 3, tid);
-      attend_step<NEG_SCALE>(st, s_cur, s_next, smem + slot * BUF_BYTES, smem + s1 * BUF_BYTES,
-                             qf, c, qr, hi);
-      if (prefetch) store_tile(smem + s2 * BUF_BYTES, nregs, p, j + 2, tid);
+      attend_step<D, NEG_SCALE>(st, s_cur, s_next, smem + slot * G::BUF, smem + s1 * G::BUF,
+                                qf, c, qr, hi);
+      if (prefetch) store_tile(smem + s2 * G::BUF, nregs, p, j + 2, tid);
       if (j + 1 <= t_hi && tile_needs_mask(p, (j + 1) * BN, w_minpos))
         mask_tile<NEG_SCALE>(s_next, p, (j + 1) * BN, my_pos, hi);
       slot = s1;
@@ -399,7 +423,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
     const float inv = empty ? 0.f : 1.0f / l;
     uint16_t* op = p.out + ro * D;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * dt + 8 * j + 4 * hi;
@@ -418,7 +442,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
     m = mtrue;
     float* op = p.part_o + ro * D;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * dt + 8 * j + 4 * hi;
@@ -436,14 +460,15 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
 
 int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
 
-// 96 KiB of dynamic LDS needs an explicit opt-in per kernel (once per process
-// and device is enough; repeating it is harmless).
-template <bool NEG>
+// More than 64 KiB of dynamic LDS needs an explicit opt-in per kernel (once
+// per process and device is enough; repeating it is harmless).
+template <int D, bool NEG>
 hipError_t launch_one(const PrefillParams& p, unsigned wgs, hipStream_t s) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NEG>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  constexpr int lds = Geo<D>::LDS;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, NEG>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_kernel<NEG>, dim3(wgs), dim3(NTHREADS), LDS_BYTES, s, p);
+  hipLaunchKernelGGL((prefill_kernel<D, NEG>), dim3(wgs), dim3(NTHREADS), lds, s, p);
   return hipGetLastError();
 }
 
@@ -482,8 +507,13 @@ hipError_t launch_prefill(const CacheView& c, const void* q, int T, int hq, int 
   p.part_l = part_l;
   const int64_t wgs = (int64_t)p.row_tiles * c.hkv * p.HGR;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-  return scale < 0.f ? launch_one<true>(p, (unsigned)wgs, s)
-                     : launch_one<false>(p, (unsigned)wgs, s);
+  if (c.head_dim == 128)
+    return scale < 0.f ? launch_one<128, true>(p, (unsigned)wgs, s)
+                       : launch_one<128, false>(p, (unsigned)wgs, s);
+  if (c.head_dim == 64)
+    return scale < 0.f ? launch_one<64, true>(p, (unsigned)wgs, s)
+                       : launch_one<64, false>(p, (unsigned)wgs, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

@@ -19,16 +19,17 @@ def lib():
     return L
 
 
-def _prompt(lib, n, hq=8, hkv=2, seed=0, pool=None, poison=True, perm_seed=None, device="cpu"):
+def _prompt(lib, n, hq=8, hkv=2, seed=0, pool=None, poison=True, perm_seed=None, device="cpu",
+            d=128):
     """A one-sequence prompt of n tokens appended into a poisoned pool."""
-    cfg = synth.prefill_config("prefill", n, 4096, 8192, hq, hkv, 128, seed_index=50 + seed,
+    cfg = synth.prefill_config("prefill", n, 4096, 8192, hq, hkv, d, seed_index=50 + seed,
                                pool_blocks=pool)
     if perm_seed is not None:
         cfg = cfg.with_(perm_seed=perm_seed)
     inp = synth.prefill_inputs(cfg, device=device)
     tables, _ = lib.build_tables([n], cfg.pool_blocks, inp["free_order"])
     td = tables.to(DEV)
-    cache = lib.PagedCache.empty(cfg.pool_blocks, hkv, 128, "bf16",
+    cache = lib.PagedCache.empty(cfg.pool_blocks, hkv, d, "bf16",
                                  fill=float("nan") if poison else None)
     seq_idx = torch.zeros(n, dtype=torch.int32, device=DEV)
     pos = torch.arange(n, dtype=torch.int32, device=DEV)
@@ -37,7 +38,8 @@ def _prompt(lib, n, hq=8, hkv=2, seed=0, pool=None, poison=True, perm_seed=None,
 
 
 def _oracle(cfg, inp, tables, hkv, heads=None):
-    dcfg = synth.decode_config("o", (cfg.prompt_len,), cfg.hq, hkv, 128, pool_blocks=cfg.pool_blocks)
+    dcfg = synth.decode_config("o", (cfg.prompt_len,), cfg.hq, hkv, cfg.head_dim,
+                               pool_blocks=cfg.pool_blocks)
     return oracle_cache(dcfg, {"k": inp["k"], "v": inp["v"]}, tables, heads=heads)
 
 
@@ -66,6 +68,34 @@ def test_prefill_final_matches_oracle(lib, T, q_pos0, kv_begin, kv_end, causal, 
     fin = np.isfinite(ref["lse"])
     assert np.array_equal(np.isfinite(gl), fin)
     assert np.abs(gl[fin] - ref["lse"][fin]).max(initial=0) < 2e-3
+
+
+@pytest.mark.parametrize("T,q_pos0,kv_begin,kv_end,causal,hq,hkv", [
+    (200, 0, 0, 200, True, 8, 2),         # whole prompt, ragged tail
+    (130, 300, 100, 357, True, 12, 4),    # unaligned shard, GQA 3
+    (90, 20, 0, 300, False, 4, 4),        # non-causal, no grouping
+])
+def test_prefill_head_dim_64(lib, T, q_pos0, kv_begin, kv_end, causal, hq, hkv):
+    n = max(kv_end, q_pos0 + T)
+    cfg, inp, tables, td, cache = _prompt(lib, n, hq=hq, hkv=hkv, seed=7, d=64)
+    q = inp["q"][q_pos0:q_pos0 + T].contiguous()
+    out, lse = lib.paged_attn_prefill(cache, q.to(DEV), q_pos0, td[0], kv_begin, kv_end, causal)
+    po, pm, pl = lib.paged_attn_prefill(cache, q.to(DEV), q_pos0, td[0], kv_begin, kv_end, causal,
+                                        partial=True)
+    torch.cuda.synchronize()
+    oc = _oracle(cfg, inp, tables, hkv)
+    ref = O.prefill(oc, bits(q), "bf16", q_pos0, tables[0], kv_begin, kv_end, causal)
+    compare_rows(out.float().cpu().numpy(), ref["o"], "bf16", f"d64 prefill {T}@{q_pos0}")
+    fin = np.isfinite(ref["lse"])
+    gl = lse.cpu().double().numpy()
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.abs(gl[fin] - ref["lse"][fin]).max(initial=0) < 2e-3
+    np.testing.assert_allclose(pm.cpu().double().numpy(), ref["m"], rtol=0, atol=1e-5)
+    pld = pl.cpu().double().numpy()
+    np.testing.assert_allclose(pld, ref["l"], rtol=2e-3)
+    live = pld > 0
+    on = np.where(live[..., None], po.cpu().double().numpy() / np.where(live, pld, 1)[..., None], 0)
+    compare_rows(on, ref["o"], "bf16", "d64 partial O~/l", out_fmt="f32")
 
 
 def test_prefill_partial_matches_oracle_state(lib):
