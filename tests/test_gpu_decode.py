@@ -180,8 +180,9 @@ def test_decode_mixed_dtypes_simple_path(lib, qd, kd):
     _decode_check(lib, cfg)
 
 
-def test_decode_fp8_with_outliers(lib):
-    cfg = synth.decode_config("fp8", (200, 64, 63, 1, 1000, 2000), 16, 2, 128, q_dtype="bf16",
+@pytest.mark.parametrize("hq,hkv,d", [(16, 2, 128), (64, 2, 64)])
+def test_decode_fp8_with_outliers(lib, hq, hkv, d):
+    cfg = synth.decode_config("fp8", (200, 64, 63, 1, 1000, 2000), hq, hkv, d, q_dtype="bf16",
                               kv_dtype="e4m3", seed_index=27, outlier_prob=0.01)
     (max_abs, row_rel), _ = _decode_check(lib, cfg)
     print(f"fp8 decode: max abs {max_abs:.2e}, row-rel {row_rel:.2e}")
@@ -221,10 +222,13 @@ def test_decode_c5_full_size_sampled(lib):
 
 
 # ------------------------------------------------------------------ merge
-@pytest.mark.parametrize("S", [1, 2, 5, 33])
-def test_lse_merge_matches_oracle(lib, S):
-    rows, D = 300, 128
-    g = torch.Generator().manual_seed(S)
+@pytest.mark.parametrize("S,D,rows", [(1, 128, 300), (2, 128, 300), (5, 128, 300), (33, 128, 300),
+                                      (3, 64, 301), (3, 96, 300), (40, 64, 300), (2100, 64, 70)])
+def test_lse_merge_matches_oracle(lib, S, D, rows):
+    """Few-part path (several rows per wave), many-part path, a head size that
+    takes the many-part path with few parts (96), and more parts than one LDS
+    chunk of weights (2100)."""
+    g = torch.Generator().manual_seed(S * 1000 + D)
     o = torch.randn(S, rows, D, generator=g) * 3
     m = torch.randn(S, rows, generator=g) * 4
     l = torch.rand(S, rows, generator=g) * 5 + 0.1
@@ -232,9 +236,9 @@ def test_lse_merge_matches_oracle(lib, S):
         m[1, :50] = -math.inf
         l[1, :50] = 0
         o[1, :50] = float("nan")
-        m[:, 290:] = -math.inf     # rows with no keys at all
-        l[:, 290:] = 0
-        o[:, 290:] = 0
+        m[:, rows - 10:] = -math.inf   # rows with no keys at all
+        l[:, rows - 10:] = 0
+        o[:, rows - 10:] = 0
     out, M, L, lse = lib.attn_lse_merge(o.to(DEV), m.to(DEV), l.to(DEV), out_dtype=torch.float32)
     torch.cuda.synchronize()
     parts = [(o[s].double().numpy(), m[s].double().numpy(), l[s].double().numpy())
