@@ -185,6 +185,7 @@ int32_t pkv_fp8_group_scales(const pkv_cache_desc* cache, const void* k_src, con
  * out: device [B][num_q_heads][head_dim] in q_dtype; out_lse: device fp32
  * [B][num_q_heads] (natural log of the softmax denominator incl. max) or NULL;
  * seq_lens: device int32 [B]; seq_lens[b] == 0 gives O = 0 and lse = -inf.
+ * B <= 65535 (larger batches: PKV_ERR_UNSUPPORTED; split the call).
  * scale == 0 means 1/sqrt(head_dim).  Requires num_q_heads % num_kv_heads == 0.
  * E4M3 caches need q_dtype PKV_BF16.  ws: device buffer of at least
  * pkv_decode_workspace_bytes(cache, q_dtype, B, num_q_heads,

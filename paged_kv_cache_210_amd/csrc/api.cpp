@@ -12,6 +12,9 @@
 
 namespace {
 
+// Sequences per decode call: the batch is the third grid dimension.
+constexpr int32_t kMaxBatch = 65535;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int elem_size(int dt) {
@@ -139,6 +142,7 @@ extern "C" int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void
   float sc;
   if (!resolve_scale(scale, cache->head_dim, &sc)) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
+  if (B > kMaxBatch) return PKV_ERR_UNSUPPORTED;
   if (!q || !block_tables || !seq_lens || !out) return PKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out)) return PKV_ERR_INVALID_ARG;
   if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE > INT32_MAX) return PKV_ERR_INVALID_ARG;
@@ -183,6 +187,7 @@ extern "C" int32_t pkv_paged_attn_decode_partial(
   float sc;
   if (!resolve_scale(scale, cache->head_dim, &sc)) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
+  if (B > kMaxBatch) return PKV_ERR_UNSUPPORTED;
   if (!q || !block_tables || !seq_lens || !part_o || !part_m || !part_l)
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(part_o)) return PKV_ERR_INVALID_ARG;

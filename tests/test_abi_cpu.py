@@ -132,6 +132,10 @@ def test_entry_point_argument_checks(lib):
     assert L.pkv_paged_attn_decode(ctypes.byref(d), 0x3000, lib.PKV_BF16, 2, 16, 0x4000, 4,
                                    0x5000, float("nan"), 0, 0x6000, None, 0x7100, 1 << 30,
                                    None) == lib.PKV_ERR_INVALID_ARG
+    # decode: batch above the grid limit
+    assert L.pkv_paged_attn_decode(ctypes.byref(d), 0x3000, lib.PKV_BF16, 65536, 16, 0x4000, 4,
+                                   0x5000, 0.0, 0, 0x6000, None, 0x7100, 1 << 40,
+                                   None) == lib.PKV_ERR_UNSUPPORTED
     # prefill: both output forms, then neither; kv range past the table
     args = (ctypes.byref(d), 0x3000, lib.PKV_BF16, 8, 16, 0, 0x4000, 4, 0, 64, 1, 0.0)
     assert L.pkv_paged_attn_prefill(*args, 0x5000, None, 0x6000, 0x7000, 0x8000,
