@@ -365,6 +365,12 @@ def cpu_baseline_prefill(cfg, budget_s, device="cuda"):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+# Blocks per decode partition: the 131072-token workload is defined with
+# 256-block partitions; the others use the library's choice (0), which for the
+# 1M-token workload is 128 partitions of 512 blocks (1024 workgroups).
+PARTITION_BLOCKS = {"C2": 0, "C3": 256, "C5": 0}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -398,7 +404,7 @@ def main(argv=None):
             rec = prefill_record(c, args.prefill_reps)
         else:
             rec, _ = decode_record(c, args.steps, args.warmup,
-                                   0 if args.only == "C2" else 256)
+                                   PARTITION_BLOCKS[args.only])
         print(json.dumps(rec), flush=True)
         return 0
     cfg = synth.CONFIGS["C2"]
@@ -410,7 +416,8 @@ def main(argv=None):
 
     secondary = []
     if not args.no_secondary:
-        for name, pb in (("C3", 256), ("C5", 256)):
+        for name in ("C3", "C5"):
+            pb = PARTITION_BLOCKS[name]
             c = synth.CONFIGS[name]
             _log(f"[bench] secondary {c.name}")
             rec, st = decode_record(c, args.steps, args.warmup, pb)

@@ -214,9 +214,10 @@ def test_decode_c3_full_size_sampled(lib):
     _decode_check(lib, cfg, partition_blocks=256, kv_heads=[0, 5], seqs=[2], device_data=DEV)
 
 
-def test_decode_c5_full_size_sampled(lib):
+@pytest.mark.parametrize("pb", [0, 256])
+def test_decode_c5_full_size_sampled(lib, pb):
     cfg = synth.CONFIGS["C5"]
-    (max_abs, row_rel), _ = _decode_check(lib, cfg, partition_blocks=256, kv_heads=[3],
+    (max_abs, row_rel), _ = _decode_check(lib, cfg, partition_blocks=pb, kv_heads=[3],
                                           device_data=DEV)
     print(f"C5 fp8 decode: max abs {max_abs:.2e}, row-rel {row_rel:.2e}")
 
