@@ -44,8 +44,10 @@ constexpr int NBUF = 3;                  // LDS ring of K/V tiles
 // Sizes for head dimension D (64 or 128).
 template <int D>
 struct Geo {
-  static constexpr int TILE = BN * D * 2;        // bytes of a K (or V) tile: 16 KiB at D 128
-  static constexpr int BUF = 2 * TILE;           // one ring slot: K tile + V tile
+  static constexpr int TILE = BN * D * 2;        // bytes of a V tile: 16 KiB at D 128
+  static constexpr int KROW = D * 2 + 16;        // K row pitch in LDS (one token, padded)
+  static constexpr int KTILE = BN * KROW;        // bytes of a K tile: 17 KiB at D 128
+  static constexpr int BUF = KTILE + TILE;       // one ring slot: K tile + V tile
   static constexpr int LDS = NBUF * BUF;
   static constexpr int PAGE = kBlock * D * 2;    // bytes of one page
   static constexpr int SPT = PAGE / 2048;        // 16-byte pieces per staging thread (128 per page)
@@ -78,13 +80,14 @@ struct PrefillParams {
   float* part_l;
 };
 
-// LDS K tile: [64 tokens][D/8 chunks of 16 B]; chunk c of token t sits at
-// c ^ f(t), f(t) = (t % 16) / (16 / (D/8)), so the 16 lanes that read one chunk
-// of 16 consecutive tokens hit 16 distinct 16-byte bank groups.
+// LDS K tile: 64 token rows of D/8 16-byte chunks, each row padded by 16
+// bytes.  The pitch (272 B at D 128, 144 B at D 64) moves consecutive rows by
+// 4 banks mod 64, so the 16 lanes that read one chunk of 16 consecutive tokens
+// hit 16 distinct 16-byte bank groups; and since the offset is a plain sum, a
+// wave reads every fragment of a tile from one base register plus constants.
 template <int D>
 __device__ __forceinline__ int k_lds_off(int t, int c) {
-  constexpr int NCH = Geo<D>::NCH;
-  return t * (D * 2) + ((c ^ ((t & 15) / (16 / NCH))) << 4);
+  return t * Geo<D>::KROW + (c << 4);
 }
 
 // LDS V tile: [4 pages][128 dims][32 B]; within a dimension the 16 tokens are
@@ -114,12 +117,15 @@ __device__ __forceinline__ int tile_entry(const PrefillParams& p, int tile, int 
 
 // Page loads of a tile.  A page past kv_end or the table, or whose entry is
 // outside the pool, is marked invalid (stored as zeros); its loads still run,
-// from block 0, so that no load sits under a branch.
+// from block 0, so that no load sits under a branch.  The two waves of a
+// 128-thread group share one page, so the page, its validity and its address
+// are wave-uniform (scalar).
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillParams& p, int tile,
                                           int entry, int tid, int kvh) {
   const int t128 = tid & 127;
-  const int lblk = tile * 4 + (tid >> 7);
+  const int lblk = __builtin_amdgcn_readfirstlane(tile * 4 + (tid >> 7));
+  entry = __builtin_amdgcn_readfirstlane(entry);        // one page per wave
   r.valid = lblk < p.maxb && lblk * kBlock < p.kv_end && (unsigned)entry < (unsigned)p.num_blocks;
   const int blk = r.valid ? entry : 0;
   const uint8_t* kp = p.k + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * kBlock * D * 2;
@@ -136,54 +142,62 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillParams& p
 // l = (o / 16) % 64 = 16g + i:
 //   K: the 8 dimensions 32c + 8g .. +8 of token i;
 //   V: tokens 4g .. 4g+3 of dimensions 32c + i and 32c + 16 + i.
+// put_piece writes piece i of this thread: K is token li, chunk 4c + g; V
+// words 0-1 are dimension 32c + li and words 2-3 dimension 32c + 16 + li,
+// tokens 4g .. 4g+3, which go to half g & 1 at byte 8 * (g >> 1).  V is
+// converted bf16 -> fp16 (exact within fp16's normal range; beyond 65504 the
+// round-toward-zero conversion saturates instead of overflowing).
+template <int D>
+__device__ __forceinline__ void put_piece(uint8_t* ks, uint8_t* vs, u32x4 kv, u32x4 vv, int i,
+                                          int pg, int t128) {
+  const int o = i * 2048 + t128 * 16;
+  const int c = o >> 10, l = (o >> 4) & 63, g = l >> 4, li = l & 15;
+  *reinterpret_cast<u32x4*>(ks + k_lds_off<D>(pg * kBlock + li, 4 * c + g)) = kv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    vv[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
+                                             __uint_as_float(vv[e] << 16),
+                                             __uint_as_float(vv[e] & 0xffff0000u)));
+  const int d0 = 32 * c + li;
+  const u32x2 a = {vv[0], vv[1]}, b = {vv[2], vv[3]};
+  *reinterpret_cast<u32x2*>(vs + v_lds_off<D>(pg, d0, g & 1) + 8 * (g >> 1)) = a;
+  *reinterpret_cast<u32x2*>(vs + v_lds_off<D>(pg, d0 + 16, g & 1) + 8 * (g >> 1)) = b;
+}
+
 // Tokens outside [kv_begin, kv_end) get zero K and V on boundary tiles, and
 // pages without a valid block are all zero, so masked positions contribute
-// exactly nothing to P V.
+// exactly nothing to P V.  Interior tiles of valid pages (all but a few) take
+// a branch with no masking at all.
 template <int D>
 __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs<D>& r,
                                            const PrefillParams& p, int tile, int tid) {
   uint8_t* ks = buf;
-  uint8_t* vs = buf + Geo<D>::TILE;
+  uint8_t* vs = buf + Geo<D>::KTILE;
   const int pg = tid >> 7, t128 = tid & 127;
   const int tok_base = tile * BN + pg * kBlock;   // first token of this page
   const bool boundary = tile * BN < p.kv_begin || tile * BN + BN > p.kv_end;
+  if (r.valid && !boundary) {                      // uniform over the wave
+#pragma unroll
+    for (int i = 0; i < Geo<D>::SPT; ++i) put_piece<D>(ks, vs, r.k[i], r.v[i], i, pg, t128);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < Geo<D>::SPT; ++i) {
     const int o = i * 2048 + t128 * 16;
-    const int c = o >> 10, l = (o >> 4) & 63, g = l >> 4, li = l & 15;
-    {  // K: token li, chunk 4c + g
-      u32x4 val = r.valid ? r.k[i] : u32x4{0u, 0u, 0u, 0u};
-      if (boundary) {
-        const int ta = tok_base + li;
-        if (ta < p.kv_begin || ta >= p.kv_end) val = u32x4{0u, 0u, 0u, 0u};
-      }
-      *reinterpret_cast<u32x4*>(ks + k_lds_off<D>(pg * kBlock + li, 4 * c + g)) = val;
-    }
-    {  // V: words 0-1 = dimension 32c + li, words 2-3 = dimension 32c + 16 + li
-      u32x4 val = r.valid ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
-      if (boundary) {
+    const int l = (o >> 4) & 63, g = l >> 4, li = l & 15;
+    u32x4 kv = r.k[i], vv = r.v[i];
+    const int ta = tok_base + li;
+    if (!r.valid || ta < p.kv_begin || ta >= p.kv_end) kv = u32x4{0u, 0u, 0u, 0u};
+    if (!r.valid) vv = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ta = tok_base + 4 * g + 2 * (e & 1);
-          uint32_t keep = 0u;
-          if (ta >= p.kv_begin && ta < p.kv_end) keep |= 0x0000ffffu;
-          if (ta + 1 >= p.kv_begin && ta + 1 < p.kv_end) keep |= 0xffff0000u;
-          val[e] &= keep;
-        }
-      }
-      // bf16 -> fp16 (exact for |v| within fp16's normal range; beyond 65504
-      // the round-toward-zero conversion saturates instead of overflowing)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        val[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
-                                                  __uint_as_float(val[e] << 16),
-                                                  __uint_as_float(val[e] & 0xffff0000u)));
-      // tokens 4g .. 4g+3 go to half g & 1 at byte 8 * (g >> 1)
-      const int d0 = 32 * c + li;
-      const u32x2 a = {val[0], val[1]}, b = {val[2], val[3]};
-      *reinterpret_cast<u32x2*>(vs + v_lds_off<D>(pg, d0, g & 1) + 8 * (g >> 1)) = a;
-      *reinterpret_cast<u32x2*>(vs + v_lds_off<D>(pg, d0 + 16, g & 1) + 8 * (g >> 1)) = b;
+    for (int e = 0; e < 4; ++e) {
+      const int tv = tok_base + 4 * g + 2 * (e & 1);
+      uint32_t keep = 0u;
+      if (tv >= p.kv_begin && tv < p.kv_end) keep |= 0x0000ffffu;
+      if (tv + 1 >= p.kv_begin && tv + 1 < p.kv_end) keep |= 0xffff0000u;
+      vv[e] &= keep;
     }
+    put_piece<D>(ks, vs, kv, vv, i, pg, t128);
   }
 }
 
@@ -307,7 +321,7 @@ __device__ __forceinline__ void attend_step(RowState<D>& st, const f32x16 (&s_cu
     }
   }
   st.l += rs;
-  const uint8_t* vs = cur + Geo<D>::TILE;
+  const uint8_t* vs = cur + Geo<D>::KTILE;
 #pragma unroll
   for (int kst = 0; kst < 4; ++kst)
 #pragma unroll
