@@ -62,6 +62,13 @@ def _decode_setup(cfg, partition_blocks):
         "seq": torch.arange(cfg.batch, dtype=torch.int32, device=dev),
         "pos": torch.tensor([n - 1 for n in lens_l], dtype=torch.int32, device=dev),
     }
+    # a second pool with the same contents: timed steps alternate between the
+    # two, so a step's pages were last read two steps earlier, with the whole
+    # other pool (1 GiB or more) read in between, and none of them is still in
+    # L2 or the last-level cache
+    twin = lib.PagedCache(cache.k.clone(), cache.v.clone(), cache.kv_dtype,
+                          None if cache.k_scale is None else cache.k_scale.clone(),
+                          None if cache.v_scale is None else cache.v_scale.clone())
     q = inp["q"]
     lens = torch.tensor(lens_l, dtype=torch.int32, device=dev)
     P = lib.decode_partitions(cache, q.dtype, cfg.batch, cfg.hq, td.shape[1], partition_blocks)
@@ -72,8 +79,8 @@ def _decode_setup(cfg, partition_blocks):
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
     del inp, keep
     torch.cuda.synchronize()
-    return dict(cache=cache, td=td, q=q, lens=lens, part=part, out=out, lse=lse,
-                step_in=step_in, tables=tables, partitions=P)
+    return dict(cache=cache, caches=(cache, twin), td=td, q=q, lens=lens, part=part, out=out,
+                lse=lse, step_in=step_in, tables=tables, partitions=P)
 
 
 def bench_decode(cfg, steps, warmup, partition_blocks=0):
@@ -81,19 +88,24 @@ def bench_decode(cfg, steps, warmup, partition_blocks=0):
 
     A step is pkv_kv_append + pkv_paged_attn_decode_partial + pkv_attn_lse_merge,
     the two launches pkv_paged_attn_decode makes, with events between them so
-    the dominant kernel is timed on its own."""
+    the dominant kernel is timed on its own.  Steps alternate between two pools
+    holding the same KV, so no step reads pages still cached from the one
+    before."""
     import torch
     from paged_kv_cache_210_amd import lib
 
     st = _decode_setup(cfg, partition_blocks)
     s = st["step_in"]
     po, pm, pl = st["part"]
+    it = [0]
 
     def step(ev=None):
-        lib.kv_append(st["cache"], s["k"], s["v"], s["seq"], s["pos"], st["td"])
+        cache = st["caches"][it[0] % 2]
+        it[0] += 1
+        lib.kv_append(cache, s["k"], s["v"], s["seq"], s["pos"], st["td"])
         if ev is not None:
             ev[0].record()
-        lib.paged_attn_decode_partial(st["cache"], st["q"], st["td"], st["lens"],
+        lib.paged_attn_decode_partial(cache, st["q"], st["td"], st["lens"],
                                       partition_blocks=partition_blocks, part=st["part"])
         if ev is not None:
             ev[1].record()
