@@ -51,7 +51,6 @@ struct Geo {
   static constexpr int LDS = NBUF * BUF;
   static constexpr int PAGE = kBlock * D * 2;    // bytes of one page
   static constexpr int SPT = PAGE / 2048;        // 16-byte pieces per staging thread (128 per page)
-  static constexpr int NCH = D / 8;              // 16-byte chunks per key
   static constexpr int QC = D / 16;              // k-steps of the score product
   static constexpr int DT = D / 32;              // 32-dimension blocks of O
 };
