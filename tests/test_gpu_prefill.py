@@ -70,6 +70,49 @@ def test_prefill_final_matches_oracle(lib, T, q_pos0, kv_begin, kv_end, causal, 
     assert np.abs(gl[fin] - ref["lse"][fin]).max(initial=0) < 2e-3
 
 
+@pytest.mark.parametrize("hq,hkv", [
+    (8, 1),      # 8 query heads per kv head: one row block of 8 heads per workgroup
+    (16, 2),     # the same with two kv heads
+    (12, 2),     # 6 per kv head: 2 heads x 4 row blocks
+    (5, 5),      # no grouping: 8 row blocks of one head
+    (10, 2),     # 5 per kv head: heads split over workgroups, 1 head x 8 row blocks
+])
+def test_prefill_gqa_groupings(lib, hq, hkv):
+    """Every way the 8 waves of a workgroup are split over heads and row
+    blocks (NH = gcd(G, 8) heads x 8 / NH row blocks), with a ragged tail and
+    an unaligned shard start."""
+    T, q_pos0, kv_begin, kv_end = 333, 170, 37, 503
+    n = max(kv_end, q_pos0 + T)
+    cfg, inp, tables, td, cache = _prompt(lib, n, hq=hq, hkv=hkv, seed=11)
+    q = inp["q"][q_pos0:q_pos0 + T].contiguous()
+    out, lse = lib.paged_attn_prefill(cache, q.to(DEV), q_pos0, td[0], kv_begin, kv_end, True)
+    torch.cuda.synchronize()
+    oc = _oracle(cfg, inp, tables, hkv)
+    ref = O.prefill(oc, bits(q), "bf16", q_pos0, tables[0], kv_begin, kv_end, True)
+    compare_rows(out.float().cpu().numpy(), ref["o"], "bf16", f"gqa {hq}/{hkv}")
+    gl = lse.cpu().double().numpy()
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.abs(gl[fin] - ref["lse"][fin]).max(initial=0) < 2e-3
+
+
+@pytest.mark.parametrize("partial", [False, True])
+def test_prefill_empty_key_range(lib, partial):
+    """kv_begin == kv_end: no row sees a key; O is exactly 0, lse -inf (final
+    form) or m = -inf and l = 0 (partial form)."""
+    n = 300
+    cfg, inp, tables, td, cache = _prompt(lib, n, seed=12)
+    q = inp["q"][100:180].contiguous().to(DEV)
+    res = lib.paged_attn_prefill(cache, q, 100, td[0], 150, 150, True, partial=partial)
+    torch.cuda.synchronize()
+    if partial:
+        po, pm, pl = res
+        assert torch.all(po == 0) and torch.all(pl == 0) and torch.all(torch.isneginf(pm))
+    else:
+        out, lse = res
+        assert torch.all(out.float() == 0) and torch.all(torch.isneginf(lse))
+
+
 @pytest.mark.parametrize("T,q_pos0,kv_begin,kv_end,causal,hq,hkv", [
     (200, 0, 0, 200, True, 8, 2),         # whole prompt, ragged tail
     (130, 300, 100, 357, True, 12, 4),    # unaligned shard, GQA 3
