@@ -206,6 +206,8 @@ def prefill_pass(cfg, st, ev=None):
     inp, td, cache, (po, pm, pl) = st["inp"], st["td"], st["cache"], st["part"]
     for c in range(cfg.num_chunks):
         a, b = c * C, min((c + 1) * C, cfg.prompt_len)
+        if ev is not None:
+            ev.append(("append", c))
         lib.kv_append(cache, inp["k"][a:b], inp["v"][a:b], st["seq"][:b - a], st["pos"][a:b], td)
         q = inp["q"][a:b]
         nsh = -(-b // S)
@@ -237,7 +239,7 @@ def prefill_record(cfg, reps):
             events[item] = e
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    attn_ms = 0.0
+    attn_ms = append_ms = 0.0
     start.record()
     for _ in range(reps):
         events.clear()
@@ -246,10 +248,14 @@ def prefill_record(cfg, reps):
         torch.cuda.synchronize()
         attn_ms += sum(events[("start", c)].elapsed_time(events[("end", c)])
                        for c in range(cfg.num_chunks))
+        append_ms += sum(events[("append", c)].elapsed_time(events[("start", c)])
+                         for c in range(cfg.num_chunks))
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end) / reps
     attn_ms /= reps
+    append_ms /= reps
+    abytes = A.append_bytes(cfg.prompt_len, cfg.hkv, cfg.head_dim, "bf16")
     flops = A.causal_prompt_flops(cfg.prompt_len, cfg.hq, cfg.head_dim)
     tflops = flops / (attn_ms * 1e-3) / 1e12
     del st
@@ -265,6 +271,9 @@ def prefill_record(cfg, reps):
                      "traffic": None,
                      "kernel": "pkv_paged_attn_prefill (all shards) + pkv_attn_lse_merge",
                      "flops_per_prompt": flops},
+        "kv_append": {"ms_per_prompt": append_ms, "bytes_per_prompt": abytes,
+                      "gbs": abytes / (append_ms * 1e-3) / 1e9,
+                      "frac_of_hbm_peak": abytes / (append_ms * 1e-3) / 1e9 / A.HBM_PEAK_GBS},
     }
 
 
@@ -446,7 +455,8 @@ def main(argv=None):
             if name == "C4" and not args.no_cpu_baseline:
                 rec["cpu_baseline"] = cpu_baseline_prefill(c, args.cpu_seconds / 2)
             secondary.append(rec)
-            _log(f"[bench]   {rec['tflops']:.0f} TFLOP/s, {rec['ms_per_prompt']:.2f} ms/prompt")
+            _log(f"[bench]   {rec['tflops']:.0f} TFLOP/s, {rec['ms_per_prompt']:.2f} ms/prompt; "
+                 f"kv_append {rec['kv_append']['gbs']:.0f} GB/s")
 
     copy = hbm_copy_record()
     _log(f"[bench] plain device copy: {copy['gbs']:.0f} GB/s")

@@ -40,12 +40,19 @@ def decode_kernel_bytes(seq_lens, hq, hkv, head_dim, q_dtype, kv_dtype):
     return kv + q + table + lens + scales
 
 
+def append_bytes(tokens, hkv, head_dim, kv_dtype, src_dtype=None):
+    """kv_append of `tokens` tokens: read each token's K and V rows, write them
+    into the pool, read its sequence index and position (table reads, one int32
+    per token at most, are left out)."""
+    src = src_dtype or ("bf16" if kv_dtype == "e4m3" else kv_dtype)
+    return tokens * hkv * head_dim * 2 * (ELEM_BYTES[src] + ELEM_BYTES[kv_dtype]) + 8 * tokens
+
+
 def decode_step_bytes(seq_lens, hq, hkv, head_dim, q_dtype, kv_dtype, src_dtype=None):
     """One decode step: append one token per sequence (read its K/V, write it
     into the pool) plus the attention read, plus writing O."""
-    src = src_dtype or ("bf16" if kv_dtype == "e4m3" else kv_dtype)
     B = len(seq_lens)
-    append = B * hkv * head_dim * 2 * (ELEM_BYTES[src] + ELEM_BYTES[kv_dtype]) + 8 * B
+    append = append_bytes(B, hkv, head_dim, kv_dtype, src_dtype)
     out = B * hq * head_dim * ELEM_BYTES[q_dtype]
     return append + decode_kernel_bytes(seq_lens, hq, hkv, head_dim, q_dtype, kv_dtype) + out
 

@@ -31,17 +31,13 @@ __device__ __forceinline__ T load_elem(const void* p, int64_t i) {
   return reinterpret_cast<const T*>(p)[i];
 }
 
-// One wave per token, four tokens per 256-thread workgroup.  Lane chunks are
-// 8 consecutive elements of the token's [Hkv][d] row; each lane issues all of
-// its loads before any store, so a small append (one token per sequence in a
-// decode step) costs about one memory round trip.  A chunk's 8 K elements
-// stay contiguous in the page (one store); its V elements are scattered (one
-// store each).  bf16 and E4M3 pages are written in fragment order, f32 pages
-// plainly ([16][d] K, [d][16] V).  Same-type caches copy raw bits; E4M3 caches
-// quantise f32(x) * f32(1/scale) with the scale of the destination
-// (block, head).
-constexpr int kChunk = 8;      // elements per lane chunk
-constexpr int kUnroll = 4;     // chunks in flight per lane
+// A chunk is 8 consecutive elements of one token's [Hkv][d] row.  Its 8 K
+// elements stay contiguous in the page (one store); its V elements are
+// scattered (one store each).  bf16 and E4M3 pages are written in fragment
+// order, f32 pages plainly ([16][d] K, [d][16] V).  Same-type caches copy raw
+// bits; E4M3 caches quantise f32(x) * f32(1/scale) with the scale of the
+// destination (block, head).
+constexpr int kChunk = 8;      // elements per chunk
 
 template <int SRC>
 struct SrcChunk;
@@ -131,34 +127,81 @@ __device__ __forceinline__ void store_chunk(const AppendParams& p, const SrcChun
   }
 }
 
+// A workgroup takes 16 consecutive input tokens and one kv head.  When the 16
+// tokens are positions p0 .. p0+15 (p0 % 16 == 0) of one sequence and the
+// page exists, the head's K and V pages are written whole: each thread moves
+// one 16-byte piece of each, the V page through an LDS transpose (bf16 pools;
+// a prefill chunk takes this path).  Otherwise each thread appends one
+// 8-element chunk of one token (store_chunk), which covers decode steps, ragged
+// ends and E4M3 / f32 pools.
+constexpr int kGroup = 16;
+
 template <int SRC, int DST>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
-  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (tok >= p.num_tokens) return;
-  const int b = p.seq_idx[tok];
-  const int pos = p.pos[tok];
-  if (b < 0 || b >= p.num_seqs || pos < 0 || (pos >> 4) >= p.maxb) return;
-  const int blk = p.tables[(int64_t)b * p.maxb + (pos >> 4)];
-  if (blk < 0 || blk >= p.num_blocks) return;
-  const int off = pos & (kBlock - 1);
+  __shared__ __attribute__((aligned(16))) uint16_t vt[128 * kGroup];   // V of one head, [d][16]
+  const int tid = threadIdx.x;
+  const int tok0 = blockIdx.x * kGroup;
+  const int h = blockIdx.y;
   const int HD = p.hkv * p.D;
-  const int nch = HD / kChunk;
-  const int64_t src0 = (int64_t)tok * HD;
-  const int64_t base = (int64_t)blk * p.block_stride;
-  for (int c0 = 0; c0 < nch; c0 += 64 * kUnroll) {
-    SrcChunk<SRC> ch[kUnroll];
+  const int cpt = p.D / kChunk;                 // chunks per token and head
+  const int t = tid / cpt, ch = tid - t * cpt;  // this thread's token and chunk
+  const int tok = tok0 + t;
+  const bool mine = t < kGroup && tok < p.num_tokens;
+  int b = -1, pos = -1;
+  if (mine) {
+    b = p.seq_idx[tok];
+    pos = p.pos[tok];
+  }
+  // whole-page test: every token is (b0, p0 + t) with p0 a page start
+  const int b0 = p.seq_idx[tok0], p0 = p.pos[tok0];
+  bool page = (DST == PKV_BF16) && tok0 + kGroup <= p.num_tokens && b0 >= 0 &&
+              b0 < p.num_seqs && p0 >= 0 && (p0 & (kBlock - 1)) == 0 && (p0 >> 4) < p.maxb;
+  int pblk = -1;
+  if (page) {
+    pblk = p.tables[(int64_t)b0 * p.maxb + (p0 >> 4)];
+    page = pblk >= 0 && pblk < p.num_blocks;
+  }
+  page = __syncthreads_and(page && (!mine || (b == b0 && pos == p0 + t))) != 0;
+
+  if constexpr (DST == PKV_BF16) {
+    if (page) {
+      const int npc = 2 * p.D;                  // 16-byte pieces per page (K or V)
+      uint8_t* kpg = p.k_pool + 2 * ((int64_t)pblk * p.block_stride + (int64_t)h * kBlock * p.D);
+      uint8_t* vpg = p.v_pool + 2 * ((int64_t)pblk * p.block_stride + (int64_t)h * p.D * kBlock);
+      const uint16_t* ksrc = static_cast<const uint16_t*>(p.k_new);
+      const uint16_t* vsrc = static_cast<const uint16_t*>(p.v_new);
+      if (tid < npc) {
+        // K piece q: token q % 16, dimensions 32 (q / 64) + 8 ((q / 16) % 4) .. +8
+        const int q = tid, c = q >> 6, g = (q >> 4) & 3, tk = q & 15;
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(
+            ksrc + (int64_t)(tok0 + tk) * HD + h * p.D + 32 * c + 8 * g);
+        *reinterpret_cast<u32x4*>(kpg + 16 * q) = kv;
+        // V: token t, dimensions 8 ch .. +8 into the [d][16] transpose
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(
+            vsrc + (int64_t)(tok0 + t) * HD + h * p.D + 8 * ch);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = c0 + u * 64 + lane;
-      if (c < nch) load_chunk<SRC>(ch[u], p.k_new, p.v_new, src0 + (int64_t)c * kChunk);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = c0 + u * 64 + lane;
-      if (c < nch) store_chunk<SRC, DST>(p, ch[u], blk, base, off, c * kChunk);
+        for (int i = 0; i < kChunk; ++i)
+          vt[(8 * ch + i) * kGroup + t] = (uint16_t)((i & 1) ? (vv[i >> 1] >> 16) : (vv[i >> 1] & 0xffffu));
+      }
+      __syncthreads();
+      if (tid < npc) {
+        // V piece q: tokens 4 ((q / 16) % 4) .. +4 of dimensions 32 (q / 64) + q % 16 and +16
+        const int q = tid, c = q >> 6, tg = (q >> 4) & 3, i = q & 15;
+        const int d0 = 32 * c + i;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(&vt[d0 * kGroup + 4 * tg]);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(&vt[(d0 + 16) * kGroup + 4 * tg]);
+        *reinterpret_cast<u32x4*>(vpg + 16 * q) = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      return;
     }
   }
+  if (!mine || b < 0 || b >= p.num_seqs || pos < 0 || (pos >> 4) >= p.maxb) return;
+  const int blk = p.tables[(int64_t)b * p.maxb + (pos >> 4)];
+  if (blk < 0 || blk >= p.num_blocks) return;
+  SrcChunk<SRC> c1;
+  const int e = h * p.D + ch * kChunk;
+  load_chunk<SRC>(c1, p.k_new, p.v_new, (int64_t)tok * HD + e);
+  store_chunk<SRC, DST>(p, c1, blk, (int64_t)blk * p.block_stride, pos & (kBlock - 1), e);
 }
 
 struct ScaleParams {
@@ -225,7 +268,8 @@ hipError_t launch_kv_append(const CacheView& c, void* k_pool, void* v_pool, cons
   AppendParams p{static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), c.block_stride,
                  c.k_scale, c.v_scale, c.num_blocks, c.hkv, c.head_dim, k_new, v_new,
                  num_tokens, seq_idx, pos, tables, num_seqs, maxb};
-  dim3 grid((num_tokens + 3) / 4), block(256);
+  if (c.head_dim > 128 || c.head_dim % kChunk) return hipErrorInvalidValue;
+  dim3 grid((num_tokens + kGroup - 1) / kGroup, c.hkv), block(256);
   if (c.kv_dtype == PKV_FP8_E4M3) {
     if (src_dtype == PKV_BF16)
       hipLaunchKernelGGL((kv_append_kernel<PKV_BF16, PKV_FP8_E4M3>), grid, block, 0, s, p);

@@ -121,6 +121,23 @@ def test_append_one_token_steps_equal_bulk(lib):
     assert torch.equal(step.v.view(torch.int16), bulk2.v.view(torch.int16))
 
 
+@pytest.mark.parametrize("d,cuts", [(64, (0, 100, 200)), (128, (0, 37, 160, 200)),
+                                     (128, (0, 16, 48, 200))])
+def test_append_in_pieces_bit_exact(lib, d, cuts):
+    """A prompt appended in pieces whose starts are page-aligned or not (whole
+    pages written at once where 16 tokens fill one, single chunks elsewhere):
+    the pool must equal the oracle's byte for byte."""
+    cfg = synth.decode_config("pieces", (200, 45), 4, 2, d, seed_index=24)
+    inp, tables, dev, tdev, cache, lens = _setup(lib, cfg, poison=False)
+    z = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16", fill=0)
+    bounds = list(cuts) + [cfg.num_tokens]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        lib.kv_append(z, dev["k"][a:b].contiguous(), dev["v"][a:b].contiguous(),
+                      dev["seq_idx"][a:b].contiguous(), dev["pos"][a:b].contiguous(), tdev)
+    torch.cuda.synchronize()
+    assert _pool_equal(z, oracle_cache(cfg, inp, tables))
+
+
 def test_append_skips_out_of_range_tokens(lib):
     cfg = synth.decode_config("skip", (20,), 4, 2, 64, seed_index=23)
     inp, tables, dev, tdev, cache, lens = _setup(lib, cfg, poison=False)
