@@ -64,6 +64,17 @@ __device__ __forceinline__ void load_chunk(SrcChunk<SRC>& c, const void* k, cons
   }
 }
 
+// 8 elements of one source array (bf16: x[0]; f32: x[0], x[1])
+template <int SRC>
+__device__ __forceinline__ void load8(u32x4 (&x)[2], const void* src, int64_t e) {
+  if constexpr (SRC == PKV_BF16) {
+    x[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + e);
+  } else {
+    x[0] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(src) + e);
+    x[1] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(src) + e + 4);
+  }
+}
+
 // element i (0..7) of a chunk as fp32
 template <int SRC>
 __device__ __forceinline__ float chunk_f32(const u32x4& x0, const u32x4* x, int i) {
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   }
   // whole-page test: every token is (b0, p0 + t) with p0 a page start
   const int b0 = p.seq_idx[tok0], p0 = p.pos[tok0];
-  bool page = (DST == PKV_BF16) && tok0 + kGroup <= p.num_tokens && b0 >= 0 &&
+  bool page = (DST != PKV_F32) && tok0 + kGroup <= p.num_tokens && b0 >= 0 &&
               b0 < p.num_seqs && p0 >= 0 && (p0 & (kBlock - 1)) == 0 && (p0 >> 4) < p.maxb;
   int pblk = -1;
   if (page) {
@@ -191,6 +202,56 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
         const u32x2 lo = *reinterpret_cast<const u32x2*>(&vt[d0 * kGroup + 4 * tg]);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(&vt[(d0 + 16) * kGroup + 4 * tg]);
         *reinterpret_cast<u32x4*>(vpg + 16 * q) = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      return;
+    }
+  }
+  if constexpr (DST == PKV_FP8_E4M3) {
+    if (page) {
+      // codes are f32(x) * f32(1 / scale) rounded to E4M3, exactly as store_chunk
+      // makes them; the V codes go through a [d][16] byte transpose
+      uint8_t* vt8 = reinterpret_cast<uint8_t*>(vt);
+      const int64_t si = (int64_t)pblk * p.hkv + h;
+      const float inv_k = __frcp_rn(p.k_scale[si]);
+      const float inv_v = __frcp_rn(p.v_scale[si]);
+      uint8_t* kpg = p.k_pool + (int64_t)pblk * p.block_stride + (int64_t)h * kBlock * p.D;
+      uint8_t* vpg = p.v_pool + (int64_t)pblk * p.block_stride + (int64_t)h * p.D * kBlock;
+      if (tid < p.D) {
+        // K piece q: token q % 16; bytes 0-7 dimensions 64 (q / 64) + 8 ((q / 16) % 4) .. +8,
+        // bytes 8-15 the same 32 dimensions further
+        const int q = tid, c2 = q >> 6, g = (q >> 4) & 3, tk = q & 15;
+        const int64_t row = (int64_t)(tok0 + tk) * HD + h * p.D;
+        u32x2 out[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 x[2] = {};
+          load8<SRC>(x, p.k_new, row + 64 * c2 + 32 * half + 8 * g);
+          u32x2 codes = {0u, 0u};
+#pragma unroll
+          for (int i = 0; i < kChunk; ++i)
+            codes[i >> 2] |= e4m3_encode(__fmul_rn(chunk_f32<SRC>(x[0], x, i), inv_k)) << (8 * (i & 3));
+          out[half] = codes;
+        }
+        *reinterpret_cast<u32x4*>(kpg + 16 * q) = u32x4{out[0].x, out[0].y, out[1].x, out[1].y};
+      }
+      if (tid < 2 * p.D) {
+        // V: token t, dimensions 8 ch .. +8 into the [d][16] transpose
+        u32x4 x[2] = {};
+        load8<SRC>(x, p.v_new, (int64_t)(tok0 + t) * HD + h * p.D + 8 * ch);
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+          vt8[(8 * ch + i) * kGroup + t] =
+              (uint8_t)e4m3_encode(__fmul_rn(chunk_f32<SRC>(x[0], x, i), inv_v));
+      }
+      __syncthreads();
+      if (tid < p.D) {
+        // V piece q: tokens 4 ((q / 16) % 4) .. +4 of dimensions 64 (q / 64) + 16 k + q % 16
+        const int q = tid, c2 = q >> 6, tg = (q >> 4) & 3, i = q & 15;
+        u32x4 pc;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          pc[k] = *reinterpret_cast<const uint32_t*>(&vt8[(64 * c2 + 16 * k + i) * kGroup + 4 * tg]);
+        *reinterpret_cast<u32x4*>(vpg + 16 * q) = pc;
       }
       return;
     }

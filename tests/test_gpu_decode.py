@@ -121,18 +121,32 @@ def test_append_one_token_steps_equal_bulk(lib):
     assert torch.equal(step.v.view(torch.int16), bulk2.v.view(torch.int16))
 
 
-@pytest.mark.parametrize("d,cuts", [(64, (0, 100, 200)), (128, (0, 37, 160, 200)),
-                                     (128, (0, 16, 48, 200))])
-def test_append_in_pieces_bit_exact(lib, d, cuts):
+@pytest.mark.parametrize("fmt,src,d,cuts", [
+    ("bf16", "bf16", 64, (0, 100, 200)),
+    ("bf16", "bf16", 128, (0, 37, 160, 200)),
+    ("bf16", "bf16", 128, (0, 16, 48, 200)),
+    ("e4m3", "bf16", 128, (0, 37, 160, 200)),
+    ("e4m3", "f32", 128, (0, 16, 48, 200)),
+    ("e4m3", "bf16", 64, (0, 100, 200)),
+])
+def test_append_in_pieces_bit_exact(lib, fmt, src, d, cuts):
     """A prompt appended in pieces whose starts are page-aligned or not (whole
     pages written at once where 16 tokens fill one, single chunks elsewhere):
-    the pool must equal the oracle's byte for byte."""
-    cfg = synth.decode_config("pieces", (200, 45), 4, 2, d, seed_index=24)
+    the pool must equal the oracle's byte for byte.  E4M3 pools are also fed
+    fp32 copies of the bf16 inputs, which must encode to the same codes."""
+    cfg = synth.decode_config("pieces", (200, 45), 4, 2, d, q_dtype="bf16", kv_dtype=fmt,
+                              seed_index=24)
     inp, tables, dev, tdev, cache, lens = _setup(lib, cfg, poison=False)
-    z = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16", fill=0)
+    z = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, fmt, fill=0)
+    if fmt == "e4m3":
+        z.k_scale.copy_(cache.k_scale)
+        z.v_scale.copy_(cache.v_scale)
+    k, v = dev["k"], dev["v"]
+    if src == "f32":
+        k, v = k.float(), v.float()
     bounds = list(cuts) + [cfg.num_tokens]
     for a, b in zip(bounds[:-1], bounds[1:]):
-        lib.kv_append(z, dev["k"][a:b].contiguous(), dev["v"][a:b].contiguous(),
+        lib.kv_append(z, k[a:b].contiguous(), v[a:b].contiguous(),
                       dev["seq_idx"][a:b].contiguous(), dev["pos"][a:b].contiguous(), tdev)
     torch.cuda.synchronize()
     assert _pool_equal(z, oracle_cache(cfg, inp, tables))
