@@ -302,7 +302,9 @@ def hbm_copy_record(reps=20, nbytes=1 << 30):
 def cpu_baseline_decode(cfg, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample of the same decode
     step: append the newest token of each sampled sequence, then attention over
-    all its keys.  Sequences are added until the budget is used."""
+    all its keys.  Sequences are added until the budget is used; when the whole
+    batch takes less, the steps are repeated over the batch (re-appending a
+    token writes the same slot with the same values) until it is used."""
     import numpy as np
     import torch
     from oracle import pkv_oracle as O
@@ -324,23 +326,37 @@ def cpu_baseline_decode(cfg, budget_s):
     q = bits(inp["q"])
     done, spent = 0, 0.0
     start = 0
+    newest = []
+
+    def timed_step(b, n, kn, vn):
+        t0 = time.perf_counter()
+        O.append(cache, kn, vn, np.array([b], np.int32), np.array([n - 1], np.int32), tables)
+        O.decode(cache, q[b:b + 1], "bf16", tables[b:b + 1], [n])
+        return time.perf_counter() - t0
+
     for b, n in enumerate(cfg.seq_lens):
         k = bits(inp["k"][start:start + n])
         v = bits(inp["v"][start:start + n])
         O.append_sequence(cache, k[:n - 1], v[:n - 1], tables[b], 0)        # untimed pre-fill
-        t0 = time.perf_counter()
-        O.append(cache, k[n - 1:n], v[n - 1:n], np.array([b], np.int32),
-                 np.array([n - 1], np.int32), tables)
-        O.decode(cache, q[b:b + 1], "bf16", tables[b:b + 1], [n])
-        spent += time.perf_counter() - t0
+        newest.append((k[n - 1:n], v[n - 1:n]))
+        spent += timed_step(b, n, *newest[b])
         done += 1
         start += n
         if spent >= budget_s:
             break
+    passes = 1
+    while spent < budget_s and done == passes * cfg.batch:
+        for b, n in enumerate(cfg.seq_lens):
+            spent += timed_step(b, n, *newest[b])
+            done += 1
+            if spent >= budget_s:
+                break
+        passes += 1
+    seqs = min(done, cfg.batch)
     return {"value": done / spent, "unit": "tok/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{done} of {cfg.batch} sequences of {cfg.name} (append newest token + "
-                      f"decode over {cfg.seq_lens[0]} keys, all {cfg.hq} heads), "
-                      f"{spent:.1f} s of CPU time",
+            "sample": f"{done} decode steps over {seqs} of {cfg.batch} sequences of {cfg.name} "
+                      f"(append newest token + decode over {cfg.seq_lens[0]} keys, all "
+                      f"{cfg.hq} heads), {spent:.1f} s of CPU time",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
