@@ -24,7 +24,9 @@
 // Workgroup = 8 waves = the NH query heads of one kv head that share K/V x NR
 // blocks of 32 query rows (NH * NR = 8).  A 64-token K/V tile (4 pages) is
 // gathered through the block table once per workgroup into a three-deep LDS
-// ring, so one barrier per tile suffices.  Each wave software-pipelines: the
+// ring, so one barrier per tile suffices: K pages go straight from memory to
+// LDS (their pool order is already the order the score product reads), V
+// pages pass through registers to be converted to fp16 and regrouped.  Each wave software-pipelines: the
 // K Q^T products of tile j+1 are issued among the softmax instructions of tile
 // j, so the matrix cores and the vector ALUs work at the same time.
 // Workgroup i serves kv head i % Hkv, so with 8 kv heads every XCD streams one
@@ -45,8 +47,7 @@ constexpr int NBUF = 3;                  // LDS ring of K/V tiles
 template <int D>
 struct Geo {
   static constexpr int TILE = BN * D * 2;        // bytes of a V tile: 16 KiB at D 128
-  static constexpr int KROW = D * 2 + 16;        // K row pitch in LDS (one token, padded)
-  static constexpr int KTILE = BN * KROW;        // bytes of a K tile: 17 KiB at D 128
+  static constexpr int KTILE = TILE;             // K tile: 4 pages as they are in the pool
   static constexpr int BUF = KTILE + TILE;       // one ring slot: K tile + V tile
   static constexpr int LDS = NBUF * BUF;
   static constexpr int PAGE = kBlock * D * 2;    // bytes of one page
@@ -79,14 +80,13 @@ struct PrefillParams {
   float* part_l;
 };
 
-// LDS K tile: 64 token rows of D/8 16-byte chunks, each row padded by 16
-// bytes.  The pitch (272 B at D 128, 144 B at D 64) moves consecutive rows by
-// 4 banks mod 64, so the 16 lanes that read one chunk of 16 consecutive tokens
-// hit 16 distinct 16-byte bank groups; and since the offset is a plain sum, a
-// wave reads every fragment of a tile from one base register plus constants.
+// LDS K tile: the tile's 4 K pages copied as they are in the pool (fragment
+// order): the 8 dimensions 32c + 8g .. +8 of token t of page pg sit at
+// pg * PAGE + c * 1024 + (16 g + t) * 16.  The 16 lanes that read one k-step
+// chunk of 16 consecutive tokens read 256 contiguous bytes.
 template <int D>
-__device__ __forceinline__ int k_lds_off(int t, int c) {
-  return t * Geo<D>::KROW + (c << 4);
+__device__ __forceinline__ int k_lds_off(int t, int k8) {    // k8: index of the 8-dim chunk
+  return (t >> 4) * Geo<D>::PAGE + (k8 >> 2) * 1024 + (((k8 & 3) << 4) + (t & 15)) * 16;
 }
 
 // LDS V tile: [4 pages][128 dims][32 B]; within a dimension the 16 tokens are
@@ -97,14 +97,16 @@ __device__ __forceinline__ int v_lds_off(int page, int d, int half) {
   return page * (D * 32) + d * 32 + ((half ^ ((d >> 3) & 1)) << 4);
 }
 
-// Staging: thread tid moves page tid / 128 of the tile, bytes
-// [i*2048 + (tid % 128)*16, +16) of that page's K and of its V (i < SPT).
+// Staging: the two waves of thread group tid / 128 take page tid / 128 of the
+// tile.  Thread tid holds bytes [i*2048 + (tid % 128)*16, +16) of that page's
+// V (i < SPT); each wave copies half of the page's K into LDS directly.
 template <int D>
 struct TileRegs {
-  u32x4 k[Geo<D>::SPT];
   u32x4 v[Geo<D>::SPT];
   bool valid;
 };
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Table entry of this thread's page (tid / 128) of a tile, read at a clamped
 // index (always in bounds; whether the page exists is decided by load_tile).
@@ -115,43 +117,62 @@ __device__ __forceinline__ int tile_entry(const PrefillParams& p, int tile, int 
 }
 
 // Page loads of a tile.  A page past kv_end or the table, or whose entry is
-// outside the pool, is marked invalid (stored as zeros); its loads still run,
-// from block 0, so that no load sits under a branch.  The two waves of a
-// 128-thread group share one page, so the page, its validity and its address
-// are wave-uniform (scalar).
+// outside the pool, is marked invalid (its V is stored as zeros; its K only
+// ever meets the mask); its loads still run, from block 0, so that no load
+// sits under a branch.  The page, its validity and its address are
+// wave-uniform (scalar).
+//
+// K is moved by global_load_lds_dwordx4: each lane's 16 bytes land at
+// M0 + 16 * lane, so one instruction fills 1 KiB of LDS.  It is issued from
+// inline assembly, which keeps M0 as it was, because the compiler treats an
+// LDS-DMA load it knows about as pending on the LDS counter and then waits
+// for every outstanding LDS read at once; opaque to it, the loads are awaited
+// with an explicit vmcnt(0) before the barrier that publishes the tile.
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillParams& p, int tile,
-                                          int entry, int tid, int kvh) {
-  const int t128 = tid & 127;
-  const int lblk = __builtin_amdgcn_readfirstlane(tile * 4 + (tid >> 7));
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, uint8_t* kdst, const PrefillParams& p,
+                                          int tile, int entry, int tid, int kvh) {
+  const int t128 = tid & 127, lane = tid & 63;
+  const int pg = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const int half = __builtin_amdgcn_readfirstlane((tid >> 6) & 1);
+  const int lblk = tile * 4 + pg;
   entry = __builtin_amdgcn_readfirstlane(entry);        // one page per wave
   r.valid = lblk < p.maxb && lblk * kBlock < p.kv_end && (unsigned)entry < (unsigned)p.num_blocks;
   const int blk = r.valid ? entry : 0;
   const uint8_t* kp = p.k + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * kBlock * D * 2;
   const uint8_t* vp = p.v + (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * D * kBlock * 2;
+  // K: this wave copies half of its page, 1 KiB per load, straight into LDS
 #pragma unroll
-  for (int i = 0; i < Geo<D>::SPT; ++i) {
-    r.k[i] = *reinterpret_cast<const u32x4*>(kp + i * 2048 + t128 * 16);
-    r.v[i] = *reinterpret_cast<const u32x4*>(vp + i * 2048 + t128 * 16);
+  for (int i = 0; i < Geo<D>::PAGE / 2048; ++i) {
+    const int o = half * (Geo<D>::PAGE / 2) + i * 1024;
+    const uint8_t* src = kp + o + lane * 16;
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void_t*)(kdst + pg * Geo<D>::PAGE + o));
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0"
+        : "=&s"(saved)
+        : "v"(src), "s"(la)
+        : "memory");
   }
+#pragma unroll
+  for (int i = 0; i < Geo<D>::SPT; ++i)
+    r.v[i] = *reinterpret_cast<const u32x4*>(vp + i * 2048 + t128 * 16);
 }
 
-// Registers -> LDS.  Pool pages are in fragment order (pkv_common.h), so a
-// 16-byte piece at byte o of a page holds, with c = o / 1024 and lane
-// l = (o / 16) % 64 = 16g + i:
-//   K: the 8 dimensions 32c + 8g .. +8 of token i;
-//   V: tokens 4g .. 4g+3 of dimensions 32c + i and 32c + 16 + i.
-// put_piece writes piece i of this thread: K is token li, chunk 4c + g; V
-// words 0-1 are dimension 32c + li and words 2-3 dimension 32c + 16 + li,
-// tokens 4g .. 4g+3, which go to half g & 1 at byte 8 * (g >> 1).  V is
-// converted bf16 -> fp16 (exact within fp16's normal range; beyond 65504 the
-// round-toward-zero conversion saturates instead of overflowing).
+// put_piece writes V piece i of this thread: words 0-1 are dimension 32c + li
+// and words 2-3 dimension 32c + 16 + li, tokens 4g .. 4g+3, which go to half
+// g & 1 at byte 8 * (g >> 1).  V is converted bf16 -> fp16 (exact within
+// fp16's normal range; beyond 65504 the round-toward-zero conversion
+// saturates instead of overflowing).
 template <int D>
-__device__ __forceinline__ void put_piece(uint8_t* ks, uint8_t* vs, u32x4 kv, u32x4 vv, int i,
-                                          int pg, int t128) {
+__device__ __forceinline__ void put_piece(uint8_t* vs, u32x4 vv, int i, int pg, int t128) {
   const int o = i * 2048 + t128 * 16;
   const int c = o >> 10, l = (o >> 4) & 63, g = l >> 4, li = l & 15;
-  *reinterpret_cast<u32x4*>(ks + k_lds_off<D>(pg * kBlock + li, 4 * c + g)) = kv;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     vv[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
@@ -163,31 +184,26 @@ __device__ __forceinline__ void put_piece(uint8_t* ks, uint8_t* vs, u32x4 kv, u3
   *reinterpret_cast<u32x2*>(vs + v_lds_off<D>(pg, d0 + 16, g & 1) + 8 * (g >> 1)) = b;
 }
 
-// Tokens outside [kv_begin, kv_end) get zero K and V on boundary tiles, and
-// pages without a valid block are all zero, so masked positions contribute
-// exactly nothing to P V.  Interior tiles of valid pages (all but a few) take
-// a branch with no masking at all.
+// V of tokens outside [kv_begin, kv_end) and of pages without a valid block
+// is stored as zeros, so masked positions contribute exactly nothing to P V
+// (their K, whatever it holds, only ever meets the mask).
 template <int D>
 __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs<D>& r,
                                            const PrefillParams& p, int tile, int tid) {
-  uint8_t* ks = buf;
   uint8_t* vs = buf + Geo<D>::KTILE;
   const int pg = tid >> 7, t128 = tid & 127;
   const int tok_base = tile * BN + pg * kBlock;   // first token of this page
   const bool boundary = tile * BN < p.kv_begin || tile * BN + BN > p.kv_end;
   if (r.valid && !boundary) {                      // uniform over the wave
 #pragma unroll
-    for (int i = 0; i < Geo<D>::SPT; ++i) put_piece<D>(ks, vs, r.k[i], r.v[i], i, pg, t128);
+    for (int i = 0; i < Geo<D>::SPT; ++i) put_piece<D>(vs, r.v[i], i, pg, t128);
     return;
   }
 #pragma unroll
   for (int i = 0; i < Geo<D>::SPT; ++i) {
     const int o = i * 2048 + t128 * 16;
-    const int l = (o >> 4) & 63, g = l >> 4, li = l & 15;
-    u32x4 kv = r.k[i], vv = r.v[i];
-    const int ta = tok_base + li;
-    if (!r.valid || ta < p.kv_begin || ta >= p.kv_end) kv = u32x4{0u, 0u, 0u, 0u};
-    if (!r.valid) vv = u32x4{0u, 0u, 0u, 0u};
+    const int l = (o >> 4) & 63, g = l >> 4;
+    u32x4 vv = r.valid ? r.v[i] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int tv = tok_base + 4 * g + 2 * (e & 1);
@@ -196,7 +212,7 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs<D>& r,
       if (tv + 1 >= p.kv_begin && tv + 1 < p.kv_end) keep |= 0xffff0000u;
       vv[e] &= keep;
     }
-    put_piece<D>(ks, vs, kv, vv, i, pg, t128);
+    put_piece<D>(vs, vv, i, pg, t128);
   }
 }
 
@@ -385,31 +401,32 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
 
   if (t_lo <= t_hi) {
     TileRegs<D> regs;
-    load_tile(regs, p, t_lo, tile_entry(p, t_lo, tid), tid, kvh);
+    load_tile(regs, smem, p, t_lo, tile_entry(p, t_lo, tid), tid, kvh);
     store_tile(smem, regs, p, t_lo, tid);
     if (t_lo + 1 <= t_hi) {
-      load_tile(regs, p, t_lo + 1, tile_entry(p, t_lo + 1, tid), tid, kvh);
+      load_tile(regs, smem + G::BUF, p, t_lo + 1, tile_entry(p, t_lo + 1, tid), tid, kvh);
       store_tile(smem + G::BUF, regs, p, t_lo + 1, tid);
     }
     int entry_next = tile_entry(p, t_lo + 2, tid);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct-to-LDS K loads are in
     __syncthreads();
 
     f32x16 sa[2], sb[2];
     qk_tile<D>(sa, smem, qf, qr, hi);
     if (tile_needs_mask(p, t_lo * BN, w_minpos)) mask_tile<NEG_SCALE>(sa, p, t_lo * BN, my_pos, hi);
 
-    // Tile j lives in ring slot (j - t_lo) % 3.  Step j loads tile j+2 into
-    // registers, attends to tile j while computing the scores of tile j+1
-    // (past the last tile those products read a stale slot and are dropped),
-    // stores tile j+2 into the slot tile j-1 left, and ends on the barrier
-    // that publishes it.
+    // Tile j lives in ring slot (j - t_lo) % 3.  Step j starts the loads of
+    // tile j+2 (K straight into the slot tile j-1 left, V into registers),
+    // attends to tile j while computing the scores of tile j+1 (past the last
+    // tile those products read a stale slot and are dropped), stores V of
+    // tile j+2, and ends on the barrier that publishes it.
     int slot = 0;
     auto step = [&](int j, const f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
       const int s1 = slot == 2 ? 0 : slot + 1;
       const int s2 = s1 == 2 ? 0 : s1 + 1;
       const bool prefetch = j + 2 <= t_hi;
       TileRegs<D> nregs;
-      if (prefetch) load_tile(nregs, p, j + 2, entry_next, tid, kvh);
+      if (prefetch) load_tile(nregs, smem + s2 * G::BUF, p, j + 2, entry_next, tid, kvh);
       entry_next = tile_entry(p, j + 3, tid);
       attend_step<D, NEG_SCALE>(st, s_cur, s_next, smem + slot * G::BUF, smem + s1 * G::BUF,
                                 qf, c, qr, hi);
@@ -417,6 +434,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
       if (j + 1 <= t_hi && tile_needs_mask(p, (j + 1) * BN, w_minpos))
         mask_tile<NEG_SCALE>(s_next, p, (j + 1) * BN, my_pos, hi);
       slot = s1;
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct-to-LDS K loads are in
       __syncthreads();
     };
     for (int j = t_lo; j <= t_hi; j += 2) {
