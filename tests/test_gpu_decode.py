@@ -152,6 +152,38 @@ def test_append_in_pieces_bit_exact(lib, fmt, src, d, cuts):
     assert _pool_equal(z, oracle_cache(cfg, inp, tables))
 
 
+def test_append_page_group_with_bad_token_falls_back(lib):
+    """16 tokens that would fill one page, but one of them names another
+    sequence (out of range) or the page's block id is invalid: the whole-page
+    path must not be taken; valid tokens are written, the others skipped."""
+    cfg = synth.decode_config("pagebad", (48,), 4, 2, 128, seed_index=33)
+    inp, tables, dev, tdev, cache, lens = _setup(lib, cfg, poison=False)
+    k, v = dev["k"][:32].contiguous(), dev["v"][:32].contiguous()
+    seq = torch.zeros(32, dtype=torch.int32, device=DEV)
+    pos = torch.arange(32, dtype=torch.int32, device=DEV)
+    seq[5] = 7                                       # not a sequence: skipped
+    z = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16", fill=0)
+    lib.kv_append(z, k, v, seq, pos, tdev)
+    bad_tab = tdev.clone()
+    bad_tab[0, 1] = cfg.pool_blocks + 3              # page 1: invalid block id
+    z2 = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16", fill=0)
+    lib.kv_append(z2, k, v, torch.zeros_like(seq), pos, bad_tab)
+    torch.cuda.synchronize()
+    # reference: the same tokens one at a time, bad ones left out
+    ref = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16", fill=0)
+    keep = [i for i in range(32) if i != 5]
+    for i in keep:
+        lib.kv_append(ref, k[i:i + 1], v[i:i + 1], seq[i:i + 1], pos[i:i + 1], tdev)
+    ref2 = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16", fill=0)
+    for i in range(16):
+        lib.kv_append(ref2, k[i:i + 1], v[i:i + 1], seq[:1] * 0, pos[i:i + 1], tdev)
+    torch.cuda.synchronize()
+    assert torch.equal(z.k.view(torch.int16), ref.k.view(torch.int16))
+    assert torch.equal(z.v.view(torch.int16), ref.v.view(torch.int16))
+    assert torch.equal(z2.k.view(torch.int16), ref2.k.view(torch.int16))
+    assert torch.equal(z2.v.view(torch.int16), ref2.v.view(torch.int16))
+
+
 def test_append_skips_out_of_range_tokens(lib):
     cfg = synth.decode_config("skip", (20,), 4, 2, 64, seed_index=23)
     inp, tables, dev, tdev, cache, lens = _setup(lib, cfg, poison=False)
