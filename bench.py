@@ -470,6 +470,7 @@ def main(argv=None):
             rec = prefill_record(c, args.prefill_reps)
             if name == "C4" and not args.no_cpu_baseline:
                 rec["cpu_baseline"] = cpu_baseline_prefill(c, args.cpu_seconds / 2)
+                rec["cpu_baseline"]["gpu_speedup"] = rec["tflops"] / rec["cpu_baseline"]["value"]
             secondary.append(rec)
             _log(f"[bench]   {rec['tflops']:.0f} TFLOP/s, {rec['ms_per_prompt']:.2f} ms/prompt; "
                  f"kv_append {rec['kv_append']['gbs']:.0f} GB/s")
@@ -481,6 +482,7 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         _log("[bench] cpu baseline (fp64 oracle)")
         cpu = cpu_baseline_decode(cfg, args.cpu_seconds)
+        cpu["gpu_speedup"] = head["tok_per_s"] / cpu["value"]
 
     line = {
         "metric": METRIC,
