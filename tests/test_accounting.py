@@ -44,6 +44,18 @@ def test_decode_bytes_of_the_workloads():
         2 ** 31 + 16384 + 262144 + 4 + 1048576
 
 
+def test_append_bytes():
+    # a 4096-token bf16 chunk, 8 kv heads, d 128: read and write 16 MiB of K and V
+    # each, plus 8 bytes of index per token
+    assert A.append_bytes(4096, 8, 128, "bf16") == 4 * 4096 * 8 * 128 * 2 + 8 * 4096
+    # E4M3 pool from bf16 sources: 2 bytes read, 1 byte written per element
+    assert A.append_bytes(10, 8, 128, "e4m3") == 10 * 8 * 128 * 2 * 3 + 80
+    # a decode step's append is the per-token term of the step bytes
+    step = A.decode_step_bytes([100, 200], 16, 4, 64, "bf16", "bf16")
+    assert step == A.append_bytes(2, 4, 64, "bf16") + \
+        A.decode_kernel_bytes([100, 200], 16, 4, 64, "bf16", "bf16") + 2 * 16 * 64 * 2
+
+
 def test_visible_pairs_brute_force():
     for (p0, T, a, b) in [(0, 10, 0, 10), (4096, 4096, 0, 8192), (4096, 4096, 8192, 16384),
                           (5, 7, 3, 9), (0, 3, 5, 9)]:
