@@ -58,6 +58,7 @@ struct Geo {
 constexpr float kLazy = 8.0f;            // log2 headroom of the running max
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 
 struct PrefillParams {
   const uint8_t* k;
@@ -325,13 +326,17 @@ __device__ __forceinline__ void attend_step(RowState<D>& st, const f32x16 (&s_cu
                                                           s_next[mt], 0, 0, 0);
     }
     const int kst = (cc * WPC) >> 3, e0 = (cc * WPC) & 7;
-#pragma unroll
-    for (int e = 0; e < WPC; ++e)
-      pb[kst][e0 + e] = (_Float16)__builtin_amdgcn_exp2f(
-          __builtin_fmaf(s_cur[kst >> 1][8 * (kst & 1) + e0 + e], c, -m_use));
+    // weights in pairs: each pair is rounded to fp16 once (round to nearest
+    // even) and that packed value feeds both P V and the row sum
 #pragma unroll
     for (int e = 0; e < WPC / 2; ++e) {
-      const f16x2 pr = {pb[kst][e0 + 2 * e], pb[kst][e0 + 2 * e + 1]};
+      const float x0 = __builtin_amdgcn_exp2f(
+          __builtin_fmaf(s_cur[kst >> 1][8 * (kst & 1) + e0 + 2 * e], c, -m_use));
+      const float x1 = __builtin_amdgcn_exp2f(
+          __builtin_fmaf(s_cur[kst >> 1][8 * (kst & 1) + e0 + 2 * e + 1], c, -m_use));
+      const f16x2 pr = __builtin_convertvector((f32x2v){x0, x1}, f16x2);
+      pb[kst][e0 + 2 * e] = pr[0];
+      pb[kst][e0 + 2 * e + 1] = pr[1];
       rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
     }
   }
