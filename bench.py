@@ -184,7 +184,7 @@ def _prefill_setup(cfg):
     inp = synth.prefill_inputs(cfg, device=dev)
     tables, _ = lib.build_tables([cfg.prompt_len], cfg.pool_blocks, inp["free_order"])
     td = tables.to(dev)
-    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16", device=dev)
+    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, cfg.kv_dtype, device=dev)
     C, S = cfg.chunk, cfg.shard_len
     max_parts = -(-cfg.prompt_len // S)
     part = (torch.empty(max_parts, C, cfg.hq, cfg.head_dim, dtype=torch.float32, device=dev),
@@ -198,8 +198,9 @@ def _prefill_setup(cfg):
 
 
 def prefill_pass(cfg, st, ev=None):
-    """One chunked pass over the prompt: per chunk append its K/V, attend to
-    each visible KV shard (partial form), merge the shards by LSE."""
+    """One chunked pass over the prompt: per chunk append its K/V (for an E4M3
+    pool: first the chunk's 64-token group scales), attend to each visible KV
+    shard (partial form), merge the shards by LSE."""
     from paged_kv_cache_210_amd import lib
 
     C, S = cfg.chunk, cfg.shard_len
@@ -208,6 +209,8 @@ def prefill_pass(cfg, st, ev=None):
         a, b = c * C, min((c + 1) * C, cfg.prompt_len)
         if ev is not None:
             ev.append(("append", c))
+        if cfg.kv_dtype == "e4m3":
+            lib.fp8_group_scales(cache, inp["k"][a:b], inp["v"][a:b], a, td[0])
         lib.kv_append(cache, inp["k"][a:b], inp["v"][a:b], st["seq"][:b - a], st["pos"][a:b], td)
         q = inp["q"][a:b]
         nsh = -(-b // S)
@@ -255,7 +258,7 @@ def prefill_record(cfg, reps):
     total_ms = start.elapsed_time(end) / reps
     attn_ms /= reps
     append_ms /= reps
-    abytes = A.append_bytes(cfg.prompt_len, cfg.hkv, cfg.head_dim, "bf16")
+    abytes = A.append_bytes(cfg.prompt_len, cfg.hkv, cfg.head_dim, cfg.kv_dtype)
     flops = A.causal_prompt_flops(cfg.prompt_len, cfg.hq, cfg.head_dim)
     tflops = flops / (attn_ms * 1e-3) / 1e12
     del st
@@ -270,8 +273,14 @@ def prefill_record(cfg, reps):
                      "unit": "TFLOP/s", "frac": tflops / A.BF16_MFMA_PEAK_TFLOPS,
                      "traffic": None,
                      "kernel": "pkv_paged_attn_prefill (all shards) + pkv_attn_lse_merge",
+                     "mfma": ("fp16 x fp16 (E4M3 tiles dequantised to fp16, q converted)"
+                              if cfg.kv_dtype == "e4m3" else "bf16 (K Q^T), fp16 (P V)"),
                      "flops_per_prompt": flops},
+        "kv_dtype": cfg.kv_dtype,
         "kv_append": {"ms_per_prompt": append_ms, "bytes_per_prompt": abytes,
+                      "includes": "kv_append" + (" + fp8_group_scales (scales read the chunk once "
+                                                 "more, not counted in bytes)"
+                                                 if cfg.kv_dtype == "e4m3" else ""),
                       "gbs": abytes / (append_ms * 1e-3) / 1e9,
                       "frac_of_hbm_peak": abytes / (append_ms * 1e-3) / 1e9 / A.HBM_PEAK_GBS},
     }
@@ -416,7 +425,7 @@ def main(argv=None):
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["C2", "C3", "C5", "C4", "C4_128K", "hbm_copy"],
+    ap.add_argument("--only", choices=["C2", "C3", "C5", "C4", "C4_128K", "C4_FP8", "hbm_copy"],
                     help="run one workload and print its record (for profiling)")
     ap.add_argument("--prefill-reps", type=int, default=2)
     args = ap.parse_args(argv)
@@ -464,7 +473,7 @@ def main(argv=None):
             secondary.append(rec)
             _log(f"[bench]   {rec['tok_per_s']:.0f} tok/s, {rec['roofline']['achieved']:.0f} GB/s")
 
-        for name in ("C4", "C4_128K"):
+        for name in ("C4", "C4_128K", "C4_FP8"):
             c = synth.CONFIGS[name]
             _log(f"[bench] secondary {c.name}")
             rec = prefill_record(c, args.prefill_reps)

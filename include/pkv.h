@@ -227,8 +227,13 @@ int32_t pkv_paged_attn_decode_partial(const pkv_cache_desc* cache, const void* q
  * Query rows q[r] (r < T) of one sequence sit at absolute positions q_pos0+r.
  * Row r attends to keys t with kv_begin <= t < kv_end and, when causal, t <=
  * q_pos0 + r, read through block_table (device int32 [max_blocks], covering
- * kv_end).  q: device [T][num_q_heads][head_dim] bf16; a bf16 cache with
- * head_dim 64 or 128 (otherwise PKV_ERR_UNSUPPORTED).
+ * kv_end).  q: device [T][num_q_heads][head_dim] bf16; a bf16 or E4M3 cache
+ * with head_dim 64 or 128 (otherwise PKV_ERR_UNSUPPORTED).  E4M3 pages [P2
+ * 3.2]: K is read as its exact codes with each page's K scale applied to the
+ * scores in fp32; V is dequantised to fp16 as it is read (f16(code * scale),
+ * one rounding); q is converted bf16 -> fp16 and both products run in fp16,
+ * so q and the dequantised V must stay within fp16's range (|x| <= 65504;
+ * beyond it q saturates and V overflows).  Scales must be positive.
  * Exactly one output form:
  *  - final:   out (device bf16 [T][num_q_heads][head_dim]) = normalised O,
  *             out_lse (nullable, fp32 [T][num_q_heads]);

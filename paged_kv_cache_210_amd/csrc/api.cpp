@@ -209,7 +209,8 @@ extern "C" int32_t pkv_paged_attn_prefill(const pkv_cache_desc* cache, const voi
                                           void* stream) {
   int32_t st = check_cache(cache);
   if (st != PKV_OK) return st;
-  if (q_dtype != PKV_BF16 || cache->kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (cache->kv_dtype != PKV_BF16 && cache->kv_dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
   if (T < 0 || num_q_heads <= 0 || q_pos0 < 0 || max_blocks <= 0) return PKV_ERR_INVALID_ARG;
   if (num_q_heads % cache->num_kv_heads) return PKV_ERR_INVALID_ARG;
   if (kv_begin < 0 || kv_end < kv_begin || (int64_t)kv_end > (int64_t)max_blocks * PKV_BLOCK_SIZE)

@@ -51,6 +51,8 @@ struct Geo {
   static constexpr int BUF = KTILE + TILE;       // one ring slot: K tile + V tile
   static constexpr int LDS = NBUF * BUF;
   static constexpr int PAGE = kBlock * D * 2;    // bytes of one page
+  static constexpr int PAGE8 = kBlock * D;       // bytes of one E4M3 page
+  static constexpr int W8 = PAGE8 / 128 / 4;     // 32-bit words of an E4M3 page per staging thread
   static constexpr int SPT = PAGE / 2048;        // 16-byte pieces per staging thread (128 per page)
   static constexpr int QC = D / 16;              // k-steps of the score product
   static constexpr int DT = D / 32;              // 32-dimension blocks of O
@@ -63,6 +65,8 @@ typedef float f32x2v __attribute__((ext_vector_type(2)));
 struct PrefillParams {
   const uint8_t* k;
   const uint8_t* v;
+  const float* k_scale;                  // E4M3 pools: [num_blocks][hkv]
+  const float* v_scale;
   int64_t block_stride_bytes;
   int num_blocks, hkv, hq, G;
   int NH, NR, HGR;                       // heads per workgroup, row blocks, head groups
@@ -217,6 +221,148 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs<D>& r,
   }
 }
 
+// ---- E4M3 pools [P2 3.2]: pages of 1-byte codes with one fp32 scale per
+// (block, kv head) for K and for V.  K codes are staged as fp16 codes (exact:
+// every E4M3 value is an fp16 value) and each page's K scale is applied to
+// its scores in fp32, so scores are as exact as for bf16 pools; the tile's
+// four K scales ride in a 16-byte LDS slot beside the ring.  V is staged
+// dequantised, f16(code * scale) (one rounding of the exact product), since
+// the scale cannot be folded into P V without also scaling the row sum.  Both
+// products then run on fp16 MFMA (q converted bf16 -> fp16 once).  fp16 must
+// hold |code * v_scale|, i.e. a V scale group's largest magnitude (<= 65504).
+// Thread tid stages words [W8 * (tid % 128), +W8) of K and of V of page
+// tid / 128.
+template <int D>
+struct TileRegs8 {
+  uint32_t k[Geo<D>::W8], v[Geo<D>::W8];
+  float ks, vs;
+  bool valid;
+};
+
+template <int D, bool F8> struct RegsOf { using T = TileRegs<D>; };
+template <int D> struct RegsOf<D, true> { using T = TileRegs8<D>; };
+
+// Two E4M3 codes (bytes 2*HI, 2*HI+1 of w) -> f16 pair of code * s.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_scaled_f16(uint32_t w, float s) {
+  f32x2v a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, HI);   // exact
+  a.x *= s;
+  a.y *= s;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(a, f16x2));   // round to nearest even
+}
+
+// Two E4M3 codes -> their exact fp16 values.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_f16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs8<D>& r, uint8_t*, const PrefillParams& p,
+                                          int tile, int entry, int tid, int kvh) {
+  const int t128 = tid & 127;
+  const int pg = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const int lblk = tile * 4 + pg;
+  entry = __builtin_amdgcn_readfirstlane(entry);        // one page per wave
+  r.valid = lblk < p.maxb && lblk * kBlock < p.kv_end && (unsigned)entry < (unsigned)p.num_blocks;
+  const int blk = r.valid ? entry : 0;
+  const int64_t pb = (int64_t)blk * p.block_stride_bytes + (int64_t)kvh * Geo<D>::PAGE8;
+  const uint8_t* kp = p.k + pb + t128 * (4 * Geo<D>::W8);
+  const uint8_t* vp = p.v + pb + t128 * (4 * Geo<D>::W8);
+  if constexpr (Geo<D>::W8 == 4) {
+    const u32x4 kk = *reinterpret_cast<const u32x4*>(kp);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(vp);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.k[j] = kk[j];
+      r.v[j] = vv[j];
+    }
+  } else {
+    const u32x2 kk = *reinterpret_cast<const u32x2*>(kp);
+    const u32x2 vv = *reinterpret_cast<const u32x2*>(vp);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      r.k[j] = kk[j];
+      r.v[j] = vv[j];
+    }
+  }
+  r.ks = p.k_scale[(int64_t)blk * p.hkv + kvh];
+  r.vs = p.v_scale[(int64_t)blk * p.hkv + kvh];
+}
+
+// K: the 8 codes of a word pair are dimensions 32c + 8g .. +8 of token t
+// (E4M3 fragment order), which become the 16-byte fp16 piece the score
+// product reads (k_lds_off); one lane per page records the page's K scale
+// (1 for a page that does not exist, whose scores are all masked).  V: a
+// word is 4 consecutive tokens of one dimension, 8 bytes of fp16 in the V
+// tile's half layout.  V of tokens outside [kv_begin, kv_end) or of an
+// invalid page is stored as zeros (selected, not multiplied, so NaN codes or
+// scales there do not leak).
+template <int D>
+__device__ __forceinline__ void store_tile(uint8_t* buf, float* ks_slot, const TileRegs8<D>& r,
+                                           const PrefillParams& p, int tile, int tid) {
+  constexpr int W8 = Geo<D>::W8;
+  uint8_t* vs = buf + Geo<D>::KTILE;
+  const int pg = tid >> 7, t128 = tid & 127;
+#pragma unroll
+  for (int q = 0; q < W8 / 2; ++q) {
+    const int o = (t128 * W8 + 2 * q) * 4;
+    const int row = (o >> 4) & 63, g = row >> 4, t = row & 15;
+    const int c = 2 * (o >> 10) + ((o >> 3) & 1);
+    const u32x4 h = {e4m3x2_f16<false>(r.k[2 * q]), e4m3x2_f16<true>(r.k[2 * q]),
+                     e4m3x2_f16<false>(r.k[2 * q + 1]), e4m3x2_f16<true>(r.k[2 * q + 1])};
+    *reinterpret_cast<u32x4*>(buf + pg * Geo<D>::PAGE + c * 1024 + ((g << 4) + t) * 16) = h;
+  }
+  if (t128 == 0) ks_slot[pg] = r.valid ? r.ks : 1.0f;
+  const int tok_base = tile * BN + pg * kBlock;   // first token of this page
+  const bool plain = r.valid && !(tile * BN < p.kv_begin || tile * BN + BN > p.kv_end);
+#pragma unroll
+  for (int j = 0; j < W8; ++j) {
+    const int o = (t128 * W8 + j) * 4;
+    const int row = (o >> 4) & 63, tg = row >> 4;
+    const int d = 16 * (4 * (o >> 10) + ((o >> 2) & 3)) + (row & 15);
+    u32x2 h = {e4m3x2_scaled_f16<false>(r.v[j], r.vs), e4m3x2_scaled_f16<true>(r.v[j], r.vs)};
+    if (!plain) {                                  // uniform over the wave
+      const int tv = tok_base + 4 * tg;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        uint32_t keep = 0u;
+        if (r.valid && tv + 2 * e >= p.kv_begin && tv + 2 * e < p.kv_end) keep |= 0x0000ffffu;
+        if (r.valid && tv + 2 * e + 1 >= p.kv_begin && tv + 2 * e + 1 < p.kv_end)
+          keep |= 0xffff0000u;
+        h[e] &= keep;
+      }
+    }
+    *reinterpret_cast<u32x2*>(vs + v_lds_off<D>(pg, d, tg & 1) + 8 * (tg >> 1)) = h;
+  }
+}
+
+// Stores a staged tile into ring slot `slot` (and, for E4M3 pools, its K
+// scales into the slot's scale entry after the ring).
+template <int D>
+__device__ __forceinline__ void stage_store(uint8_t* smem, int slot, const TileRegs<D>& r,
+                                            const PrefillParams& p, int tile, int tid) {
+  store_tile(smem + slot * Geo<D>::BUF, r, p, tile, tid);
+}
+template <int D>
+__device__ __forceinline__ void stage_store(uint8_t* smem, int slot, const TileRegs8<D>& r,
+                                            const PrefillParams& p, int tile, int tid) {
+  store_tile(smem + slot * Geo<D>::BUF,
+             reinterpret_cast<float*>(smem + Geo<D>::LDS + 16 * slot), r, p, tile, tid);
+}
+
+// Score product S^T = K Q^T: bf16 operands for bf16 pools, fp16 for E4M3
+// pools (dequantised tile, converted q).
+template <bool F8>
+__device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (F8)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 template <int D>
 struct RowState {
   f32x16 o[Geo<D>::DT];   // O^T[32*dt + 8*(r/4) + 4*(lane/32) + r%4][row]
@@ -225,7 +371,7 @@ struct RowState {
 };
 
 // S^T for one tile: s[mt][r] = score of key 32*mt + 8*(r/4) + 4*hi + r%4.
-template <int D>
+template <int D, bool F8>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const uint8_t* ks,
                                         const u32x4 (&qf)[Geo<D>::QC], int qr, int hi) {
 #pragma unroll
@@ -237,9 +383,7 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const uint8_t* ks,
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + k_lds_off<D>(32 * mt + qr, 2 * c + hi));
-      s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                     __builtin_bit_cast(bf16x8, qf[c]), s[mt], 0,
-                                                     0, 0);
+      s[mt] = mfma_qk<F8>(kf, qf[c], s[mt]);
     }
 }
 
@@ -295,19 +439,62 @@ __device__ __forceinline__ float update_max(RowState<D>& st, const f32x16 (&s)[2
   return st.m == -INFINITY ? 0.f : st.m;
 }
 
+// The same for an E4M3 tile, whose page i carries its own K scale: cp[i] =
+// c * k_scale (same sign as c, as scales are positive), so each page's
+// extreme raw score is scaled by its own multiplier.
+template <int D, bool NEG_SCALE>
+__device__ __forceinline__ float update_max_paged(RowState<D>& st, const f32x16 (&s)[2],
+                                                  const float (&cp)[4]) {
+  const float hidden = NEG_SCALE ? INFINITY : -INFINITY;
+  float lmx = -INFINITY;
+#pragma unroll
+  for (int pg = 0; pg < 4; ++pg) {          // page pg holds s[pg / 2][8 * (pg % 2) .. +8]
+    float ext = hidden;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float x = s[pg >> 1][8 * (pg & 1) + r];
+      ext = NEG_SCALE ? fminf(ext, x) : fmaxf(ext, x);
+    }
+    lmx = fmaxf(lmx, ext == hidden ? -INFINITY : ext * cp[pg]);
+  }
+  st.mtrue = fmaxf(st.mtrue, lmx);
+  if (__ballot(lmx > st.m + kLazy) != 0ull) {
+    const float mx = fmaxf(lmx, __shfl_xor(lmx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < Geo<D>::DT; ++dt) st.o[dt] *= alpha;
+    st.m = m_new;
+  }
+  return st.m == -INFINITY ? 0.f : st.m;
+}
+
 // One pipelined step of a wave: the scores s_cur of tile j (already masked)
 // become fp16 weights while the K Q^T products of tile j+1 (LDS buffer nxt)
 // run into s_next, then O^T += V^T P^T for tile j.  The row sum is taken over
 // the rounded weights that enter the product, so the result stays an exact
 // weighted average of V rows.
-template <int D, bool NEG_SCALE>
+template <int D, bool NEG_SCALE, bool F8>
 __device__ __forceinline__ void attend_step(RowState<D>& st, const f32x16 (&s_cur)[2],
                                             f32x16 (&s_next)[2], const uint8_t* cur,
                                             const uint8_t* nxt, const u32x4 (&qf)[Geo<D>::QC],
-                                            float c, int qr, int hi) {
+                                            float c, const float* ks_cur, int qr, int hi) {
   constexpr int QC = Geo<D>::QC;
   constexpr int WPC = 32 / QC;          // weights made per k-step of the score product
-  const float m_use = update_max<D, NEG_SCALE>(st, s_cur, c);
+  // score multiplier of k-step (= page) i: c, times the page's K scale for E4M3
+  float cp[4];
+  float m_use;
+  if constexpr (F8) {
+    const f32x4 kv = *reinterpret_cast<const f32x4*>(ks_cur);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cp[i] = c * kv[i];
+    m_use = update_max_paged<D, NEG_SCALE>(st, s_cur, cp);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cp[i] = c;
+    m_use = update_max<D, NEG_SCALE>(st, s_cur, c);
+  }
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -321,9 +508,7 @@ __device__ __forceinline__ void attend_step(RowState<D>& st, const f32x16 (&s_cu
     for (int mt = 0; mt < 2; ++mt) {
       const u32x4 kf =
           *reinterpret_cast<const u32x4*>(nxt + k_lds_off<D>(32 * mt + qr, 2 * cc + hi));
-      s_next[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                          __builtin_bit_cast(bf16x8, qf[cc]),
-                                                          s_next[mt], 0, 0, 0);
+      s_next[mt] = mfma_qk<F8>(kf, qf[cc], s_next[mt]);
     }
     const int kst = (cc * WPC) >> 3, e0 = (cc * WPC) & 7;
     // weights in pairs: each pair is rounded to fp16 once (round to nearest
@@ -331,9 +516,9 @@ __device__ __forceinline__ void attend_step(RowState<D>& st, const f32x16 (&s_cu
 #pragma unroll
     for (int e = 0; e < WPC / 2; ++e) {
       const float x0 = __builtin_amdgcn_exp2f(
-          __builtin_fmaf(s_cur[kst >> 1][8 * (kst & 1) + e0 + 2 * e], c, -m_use));
+          __builtin_fmaf(s_cur[kst >> 1][8 * (kst & 1) + e0 + 2 * e], cp[kst], -m_use));
       const float x1 = __builtin_amdgcn_exp2f(
-          __builtin_fmaf(s_cur[kst >> 1][8 * (kst & 1) + e0 + 2 * e + 1], c, -m_use));
+          __builtin_fmaf(s_cur[kst >> 1][8 * (kst & 1) + e0 + 2 * e + 1], cp[kst], -m_use));
       const f16x2 pr = __builtin_convertvector((f32x2v){x0, x1}, f16x2);
       pb[kst][e0 + 2 * e] = pr[0];
       pb[kst][e0 + 2 * e + 1] = pr[1];
@@ -352,9 +537,10 @@ __device__ __forceinline__ void attend_step(RowState<D>& st, const f32x16 (&s_cu
     }
 }
 
-template <int D, bool NEG_SCALE>
+template <int D, bool NEG_SCALE, bool F8>
 __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
   using G = Geo<D>;
+  using Regs = typename RegsOf<D, F8>::T;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -376,14 +562,23 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
   const bool row_ok = my_row < p.T;
   const int my_pos = p.q_pos0 + my_row;
 
-  // query fragments (B operand): Q[row][16c + 8*hi .. +8]
+  // query fragments (B operand): Q[row][16c + 8*hi .. +8]; for E4M3 pools
+  // converted to fp16 (exact for bf16 values within fp16's range)
   u32x4 qf[G::QC];
   {
     const uint16_t* qp = p.q + ((int64_t)my_row * p.hq + h) * D;
 #pragma unroll
-    for (int c = 0; c < G::QC; ++c)
+    for (int c = 0; c < G::QC; ++c) {
       qf[c] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * c + 8 * hi)
                      : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (F8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qf[c][e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
+                                                      __uint_as_float(qf[c][e] << 16),
+                                                      __uint_as_float(qf[c][e] & 0xffff0000u)));
+      }
+    }
   }
 
   // keys this workgroup may see
@@ -405,19 +600,19 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
   const float c = p.scale_log2;
 
   if (t_lo <= t_hi) {
-    TileRegs<D> regs;
+    Regs regs;
     load_tile(regs, smem, p, t_lo, tile_entry(p, t_lo, tid), tid, kvh);
-    store_tile(smem, regs, p, t_lo, tid);
+    stage_store(smem, 0, regs, p, t_lo, tid);
     if (t_lo + 1 <= t_hi) {
       load_tile(regs, smem + G::BUF, p, t_lo + 1, tile_entry(p, t_lo + 1, tid), tid, kvh);
-      store_tile(smem + G::BUF, regs, p, t_lo + 1, tid);
+      stage_store(smem, 1, regs, p, t_lo + 1, tid);
     }
     int entry_next = tile_entry(p, t_lo + 2, tid);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct-to-LDS K loads are in
     __syncthreads();
 
     f32x16 sa[2], sb[2];
-    qk_tile<D>(sa, smem, qf, qr, hi);
+    qk_tile<D, F8>(sa, smem, qf, qr, hi);
     if (tile_needs_mask(p, t_lo * BN, w_minpos)) mask_tile<NEG_SCALE>(sa, p, t_lo * BN, my_pos, hi);
 
     // Tile j lives in ring slot (j - t_lo) % 3.  Step j starts the loads of
@@ -430,12 +625,13 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
       const int s1 = slot == 2 ? 0 : slot + 1;
       const int s2 = s1 == 2 ? 0 : s1 + 1;
       const bool prefetch = j + 2 <= t_hi;
-      TileRegs<D> nregs;
+      Regs nregs;
       if (prefetch) load_tile(nregs, smem + s2 * G::BUF, p, j + 2, entry_next, tid, kvh);
       entry_next = tile_entry(p, j + 3, tid);
-      attend_step<D, NEG_SCALE>(st, s_cur, s_next, smem + slot * G::BUF, smem + s1 * G::BUF,
-                                qf, c, qr, hi);
-      if (prefetch) store_tile(smem + s2 * G::BUF, nregs, p, j + 2, tid);
+      attend_step<D, NEG_SCALE, F8>(st, s_cur, s_next, smem + slot * G::BUF, smem + s1 * G::BUF,
+                                    qf, c, reinterpret_cast<const float*>(smem + G::LDS + 16 * slot),
+                                    qr, hi);
+      if (prefetch) stage_store(smem, s2, nregs, p, j + 2, tid);
       if (j + 1 <= t_hi && tile_needs_mask(p, (j + 1) * BN, w_minpos))
         mask_tile<NEG_SCALE>(s_next, p, (j + 1) * BN, my_pos, hi);
       slot = s1;
@@ -498,14 +694,19 @@ int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
 
 // More than 64 KiB of dynamic LDS needs an explicit opt-in per kernel (once
 // per process and device is enough; repeating it is harmless).
-template <int D, bool NEG>
+template <int D, bool NEG, bool F8>
 hipError_t launch_one(const PrefillParams& p, unsigned wgs, hipStream_t s) {
-  constexpr int lds = Geo<D>::LDS;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, NEG>),
+  constexpr int lds = Geo<D>::LDS + (F8 ? 16 * NBUF : 0);   // E4M3: K scales of each slot
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, NEG, F8>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_kernel<D, NEG>), dim3(wgs), dim3(NTHREADS), lds, s, p);
+  hipLaunchKernelGGL((prefill_kernel<D, NEG, F8>), dim3(wgs), dim3(NTHREADS), lds, s, p);
   return hipGetLastError();
+}
+
+template <int D, bool F8>
+hipError_t launch_sign(const PrefillParams& p, unsigned wgs, float scale, hipStream_t s) {
+  return scale < 0.f ? launch_one<D, true, F8>(p, wgs, s) : launch_one<D, false, F8>(p, wgs, s);
 }
 
 }  // namespace
@@ -518,7 +719,10 @@ hipError_t launch_prefill(const CacheView& c, const void* q, int T, int hq, int 
   PrefillParams p{};
   p.k = static_cast<const uint8_t*>(c.k);
   p.v = static_cast<const uint8_t*>(c.v);
-  p.block_stride_bytes = c.block_stride * 2;
+  const bool f8 = c.kv_dtype == PKV_FP8_E4M3;
+  p.k_scale = c.k_scale;
+  p.v_scale = c.v_scale;
+  p.block_stride_bytes = c.block_stride * (f8 ? 1 : 2);
   p.num_blocks = c.num_blocks;
   p.hkv = c.hkv;
   p.hq = hq;
@@ -544,11 +748,11 @@ hipError_t launch_prefill(const CacheView& c, const void* q, int T, int hq, int 
   const int64_t wgs = (int64_t)p.row_tiles * c.hkv * p.HGR;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   if (c.head_dim == 128)
-    return scale < 0.f ? launch_one<128, true>(p, (unsigned)wgs, s)
-                       : launch_one<128, false>(p, (unsigned)wgs, s);
+    return f8 ? launch_sign<128, true>(p, (unsigned)wgs, scale, s)
+              : launch_sign<128, false>(p, (unsigned)wgs, scale, s);
   if (c.head_dim == 64)
-    return scale < 0.f ? launch_one<64, true>(p, (unsigned)wgs, s)
-                       : launch_one<64, false>(p, (unsigned)wgs, s);
+    return f8 ? launch_sign<64, true>(p, (unsigned)wgs, scale, s)
+              : launch_sign<64, false>(p, (unsigned)wgs, scale, s);
   return hipErrorInvalidValue;
 }
 

@@ -61,10 +61,15 @@ class PrefillConfig:
     hq: int
     hkv: int
     head_dim: int
-    dtype: str              # "bf16"
+    dtype: str              # "bf16" (q, and the K/V source values)
     pool_blocks: int
     data_seed: int = 1000
     perm_seed: int = 2000
+    kv_dtype: str = "bf16"  # "bf16" | "e4m3" (pool format)
+    outlier_seed: int = 3000
+    outlier_prob: float = 0.0
+    outlier_mult: float = 8.0
+    scale_group: int = 64          # tokens per FP8 scale (e4m3 only)
     block_size: int = BLOCK_SIZE
 
     @property
@@ -92,12 +97,13 @@ def decode_config(name, seq_lens, hq, hkv, head_dim, q_dtype="bf16", kv_dtype=No
 
 
 def prefill_config(name, prompt_len, chunk, shard_len, hq, hkv, head_dim, dtype="bf16",
-                   pool_blocks=None, seed_index=0) -> PrefillConfig:
+                   pool_blocks=None, seed_index=0, **kw) -> PrefillConfig:
     if pool_blocks is None:
         pool_blocks = pool_with_spare(blocks_needed([prompt_len]))
     return PrefillConfig(name=name, prompt_len=prompt_len, chunk=chunk, shard_len=shard_len,
                          hq=hq, hkv=hkv, head_dim=head_dim, dtype=dtype, pool_blocks=pool_blocks,
-                         data_seed=1000 + seed_index, perm_seed=2000 + seed_index)
+                         data_seed=1000 + seed_index, perm_seed=2000 + seed_index,
+                         outlier_seed=3000 + seed_index, **kw)
 
 
 CONFIGS = {
@@ -111,6 +117,11 @@ CONFIGS = {
                          seed_index=4),
     "C4_128K": prefill_config("C4 chunked causal prefill 131072", 131072, 4096, 32768, 32, 8,
                               128, seed_index=6),
+    # the 32K chunked prefill over an E4M3 pool (the FP8 KV format of the 1M
+    # decode: one scale per 64 tokens per kv head, 1 % of values x8)
+    "C4_FP8": prefill_config("C4 chunked causal prefill 32768, E4M3 KV", 32768, 4096, 8192, 32,
+                             8, 128, seed_index=7, kv_dtype="e4m3", outlier_prob=0.01,
+                             outlier_mult=8.0),
     "C5": decode_config("C5 1M-context FP8-KV decode", (1048576,), 64, 8, 128, q_dtype="bf16",
                         kv_dtype="e4m3", partition_blocks=256, seed_index=5,
                         outlier_prob=0.01, outlier_mult=8.0),

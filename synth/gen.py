@@ -45,6 +45,16 @@ def _randn(shape, g, device):
     return torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
 
 
+def _outliers(cfg, k, v, device):
+    go = generator(cfg.outlier_seed, device)
+    mk = torch.rand(k.shape, generator=go, device=device) < cfg.outlier_prob
+    k = torch.where(mk, k * cfg.outlier_mult, k)
+    del mk
+    mv = torch.rand(v.shape, generator=go, device=device) < cfg.outlier_prob
+    v = torch.where(mv, v * cfg.outlier_mult, v)
+    return k, v
+
+
 def decode_inputs(cfg, device="cpu"):
     """q [B,Hq,d], k/v [T,Hkv,d] for every token of every sequence, seq_idx/pos [T].
 
@@ -55,13 +65,7 @@ def decode_inputs(cfg, device="cpu"):
     k = _randn((T, cfg.hkv, cfg.head_dim), g, device)
     v = _randn((T, cfg.hkv, cfg.head_dim), g, device)
     if cfg.outlier_prob > 0:
-        go = generator(cfg.outlier_seed, device)
-        mk = torch.rand(k.shape, generator=go, device=device) < cfg.outlier_prob
-        k = torch.where(mk, k * cfg.outlier_mult, k)
-        del mk
-        mv = torch.rand(v.shape, generator=go, device=device) < cfg.outlier_prob
-        v = torch.where(mv, v * cfg.outlier_mult, v)
-        del mv
+        k, v = _outliers(cfg, k, v, device)
     src_dt = _DT["bf16"] if cfg.kv_dtype == "e4m3" else _DT[cfg.kv_dtype]
     seq_idx, pos = token_positions(cfg.seq_lens)
     return {
@@ -79,7 +83,9 @@ def prefill_inputs(cfg, device="cpu"):
     g = generator(cfg.data_seed, device)
     S = cfg.prompt_len
     q = _randn((S, cfg.hq, cfg.head_dim), g, device).to(_DT[cfg.dtype])
-    k = _randn((S, cfg.hkv, cfg.head_dim), g, device).to(_DT[cfg.dtype])
-    v = _randn((S, cfg.hkv, cfg.head_dim), g, device).to(_DT[cfg.dtype])
-    return {"q": q, "k": k, "v": v,
+    k = _randn((S, cfg.hkv, cfg.head_dim), g, device)
+    v = _randn((S, cfg.hkv, cfg.head_dim), g, device)
+    if cfg.outlier_prob > 0:
+        k, v = _outliers(cfg, k, v, device)
+    return {"q": q, "k": k.to(_DT[cfg.dtype]), "v": v.to(_DT[cfg.dtype]),
             "free_order": free_order(cfg.pool_blocks, cfg.perm_seed)}
