@@ -286,6 +286,61 @@ def prefill_record(cfg, reps):
     }
 
 
+def block_copy_record(reps=5, blocks=8192, cow_blocks=32):
+    """pkv_copy_blocks on the Llama-3-8B-like layer's pool layout (8 kv heads,
+    d 128, bf16: 64 KiB per block): offload of `blocks` blocks from HBM to a
+    pinned host pool and page-in back (PCIe-bound), the same number copied
+    inside HBM, and one copy-on-write launch of `cow_blocks` single blocks (one
+    per sequence after a fork).  Times are HIP events on the launching stream."""
+    import torch
+    from paged_kv_cache_210_amd import accounting as A
+    from paged_kv_cache_210_amd import lib
+
+    hkv, d = 8, 128
+    nb = 2 * blocks
+    dev = lib.PagedCache.empty(nb, hkv, d, "bf16")
+    dev.k.normal_()
+    dev.v.normal_()
+    host = lib.PagedCache.empty(blocks, hkv, d, "bf16", pinned=True)
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    src, dst = perm[:blocks].cuda(), perm[blocks:].cuda()
+    slots = torch.arange(blocks, dtype=torch.int32, device="cuda")
+    per_block = A.block_bytes(hkv, d, "bf16")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out_ms = timed(lambda: lib.copy_blocks(dev, host, src, slots))
+    in_ms = timed(lambda: lib.copy_blocks(host, dev, slots, dst))
+    hbm_ms = timed(lambda: lib.copy_blocks(dev, dev, src, dst))
+    cow_ms = timed(lambda: lib.copy_blocks(dev, dev, src[:cow_blocks], dst[:cow_blocks]))
+    moved = blocks * per_block
+    rec = {
+        "workload": f"pkv_copy_blocks, {blocks} blocks of 8 kv heads x d 128 bf16 "
+                    f"({moved / 2**20:.0f} MiB), random block ids",
+        "offload_gbs": moved / (out_ms * 1e-3) / 1e9,
+        "page_in_gbs": moved / (in_ms * 1e-3) / 1e9,
+        "pcie_peak_gbs": A.PCIE_PEAK_GBS,
+        "offload_frac_of_pcie": moved / (out_ms * 1e-3) / 1e9 / A.PCIE_PEAK_GBS,
+        "page_in_frac_of_pcie": moved / (in_ms * 1e-3) / 1e9 / A.PCIE_PEAK_GBS,
+        "hbm_copy_gbs_read_plus_write": 2 * moved / (hbm_ms * 1e-3) / 1e9,
+        "hbm_frac": 2 * moved / (hbm_ms * 1e-3) / 1e9 / A.HBM_PEAK_GBS,
+        "cow_launch_us": cow_ms * 1e3,
+        "cow_blocks": cow_blocks,
+    }
+    del dev, host
+    torch.cuda.empty_cache()
+    return rec
+
+
 def hbm_copy_record(reps=20, nbytes=1 << 30):
     """A plain device-to-device copy of a known size: the attainable-bandwidth
     context for the decode roofline, and the reference kernel for scaling the
@@ -425,7 +480,8 @@ def main(argv=None):
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["C2", "C3", "C5", "C4", "C4_128K", "C4_FP8", "hbm_copy"],
+    ap.add_argument("--only", choices=["C2", "C3", "C5", "C4", "C4_128K", "C4_FP8", "hbm_copy",
+                                       "block_copy"],
                     help="run one workload and print its record (for profiling)")
     ap.add_argument("--prefill-reps", type=int, default=2)
     args = ap.parse_args(argv)
@@ -442,6 +498,9 @@ def main(argv=None):
     torch.cuda.init()
     if args.only == "hbm_copy":
         print(json.dumps(hbm_copy_record(args.steps)), flush=True)
+        return 0
+    if args.only == "block_copy":
+        print(json.dumps(block_copy_record()), flush=True)
         return 0
     if args.only:
         c = synth.CONFIGS[args.only]
@@ -483,6 +542,12 @@ def main(argv=None):
             secondary.append(rec)
             _log(f"[bench]   {rec['tflops']:.0f} TFLOP/s, {rec['ms_per_prompt']:.2f} ms/prompt; "
                  f"kv_append {rec['kv_append']['gbs']:.0f} GB/s")
+
+    if not args.no_secondary:
+        bc = block_copy_record()
+        secondary.append(bc)
+        _log(f"[bench] block copies: offload {bc['offload_gbs']:.1f} GB/s, page-in "
+             f"{bc['page_in_gbs']:.1f} GB/s, in HBM {bc['hbm_copy_gbs_read_plus_write']:.0f} GB/s")
 
     copy = hbm_copy_record()
     _log(f"[bench] plain device copy: {copy['gbs']:.0f} GB/s")

@@ -59,7 +59,9 @@ enum {
   PKV_ERR_NO_BLOCKS = -3,    /* allocator has too few free blocks            */
   PKV_ERR_WORKSPACE = -4,    /* workspace missing or too small               */
   PKV_ERR_DEVICE = -5,       /* a HIP runtime call failed                    */
-  PKV_ERR_BAD_TABLE = -6     /* pkv_validate_tables found a bad entry        */
+  PKV_ERR_BAD_TABLE = -6,    /* pkv_validate_tables found a bad entry        */
+  PKV_ERR_SHARED = -7        /* a write would land in a block another table
+                                holds (use pkv_allocator_reserve_cow)        */
 };
 
 /* ---- element types ----------------------------------------------------- */
@@ -131,12 +133,44 @@ int32_t pkv_allocator_create(int32_t num_blocks, const int32_t* free_order,
 int32_t pkv_allocator_reserve(pkv_allocator* a, int32_t seq, int64_t new_len,
                               int32_t* table_row, int32_t max_blocks,
                               int32_t* num_blocks_out);
-/* Return all of seq's blocks to the free list and forget the sequence. */
+/* Forget the sequence; each of its blocks is released, and returns to the
+ * back of the free list (in table order) when no other table holds it. */
 int32_t pkv_allocator_release(pkv_allocator* a, int32_t seq);
 /* Unused slots in seq's last block (0 for an unknown sequence). */
 int32_t pkv_allocator_waste_slots(const pkv_allocator* a, int32_t seq, int64_t* out);
 int32_t pkv_allocator_free_count(const pkv_allocator* a, int32_t* out);
 void pkv_allocator_destroy(pkv_allocator* a);
+
+/* ---- prefix sharing [P2 3.1 copy-on-write; P1 5 prefix cache] -------------
+ * Every block counts the tables that hold it (pkv_allocator_refcount; 0 for a
+ * free block).  pkv_allocator_reserve refuses (PKV_ERR_SHARED, nothing
+ * changed) a growth that would write into a partly filled last block that
+ * another table also holds; pkv_allocator_reserve_cow then first moves this
+ * sequence onto a fresh block (taken from the free list before the growth's
+ * own blocks; all-or-nothing as well) and reports the pair: *cow_src = the
+ * shared block, *cow_dst = the fresh one, whose contents the caller copies
+ * with pkv_copy_blocks before appending (-1, -1 when no copy is needed).
+ * Kernels read shared blocks like any other: tables may alias blocks that
+ * are only read. */
+int32_t pkv_allocator_reserve_cow(pkv_allocator* a, int32_t seq, int64_t new_len,
+                                  int32_t* table_row, int32_t max_blocks,
+                                  int32_t* num_blocks_out, int32_t* cow_src, int32_t* cow_dst);
+/* New sequence dst_seq (must not exist) holding every block of src_seq (which
+ * must exist), with its length. */
+int32_t pkv_allocator_fork(pkv_allocator* a, int32_t src_seq, int32_t dst_seq);
+/* Publish seq's first n_full blocks (all full: n_full*16 <= its length) under
+ * block_hashes[j], a caller-computed hash of tokens [0, 16(j+1)) of the prompt
+ * (chained, so equal hashes mean equal prefixes).  A hash or block already
+ * published keeps its first entry.  A block leaves the index when it is
+ * freed. */
+int32_t pkv_allocator_publish_prefix(pkv_allocator* a, int32_t seq, const uint64_t* block_hashes,
+                                     int32_t n_full);
+/* For a sequence that does not exist yet (or holds nothing): take the longest
+ * run block_hashes[0..] of published blocks, in order; the sequence then holds
+ * them and has length 16 * *matched (its prefill starts at that token). */
+int32_t pkv_allocator_match_prefix(pkv_allocator* a, int32_t seq, const uint64_t* block_hashes,
+                                   int32_t n, int32_t* matched);
+int32_t pkv_allocator_refcount(const pkv_allocator* a, int32_t block, int32_t* out);
 
 /* ---- kv_append: write new tokens into pool slots [P1 2.2] ----------------
  * For token i < num_tokens: block = block_tables[seq_idx[i]*max_blocks_per_seq
@@ -263,11 +297,27 @@ int32_t pkv_attn_lse_merge(int32_t S, int64_t rows, int32_t head_dim, const floa
                            int32_t out_dtype, float* out_m, float* out_l, float* out_lse,
                            void* stream);
 
+/* ---- whole-block copies: copy-on-write and offload [P2 3.1; P1 4] --------
+ * For i < n: every kv head's K and V page of block src_ids[i] of pool `src` is
+ * copied bit for bit to block dst_ids[i] of pool `dst`, with its K and V
+ * scales for E4M3 pools.  src and dst have the same kv_dtype, num_kv_heads and
+ * head_dim (block_stride may differ; they may be one pool).  Either pool may
+ * be device memory or pinned host memory that the device can address
+ * (hipHostMalloc): device -> host moves blocks out of HBM (offload), host ->
+ * device brings them back, device -> device serves copy-on-write.
+ * src_ids, dst_ids: int32 [n] in memory the device can read.  A pair with an
+ * id outside its pool is skipped.  Destinations must be distinct and must not
+ * be sources of the same call (such copies race). */
+int32_t pkv_copy_blocks(const pkv_cache_desc* src, const pkv_cache_desc* dst,
+                        const int32_t* src_ids, const int32_t* dst_ids, int32_t n, void* stream);
+
 /* ---- table check (debug) ---------------------------------------------------
  * Copies block_tables / seq_lens (device) to the host after synchronising
  * `stream`, and checks that every entry covered by seq_lens[b] (the first
  * ceil(seq_lens[b]/16)) is in [0, num_blocks) and that no physical block is
- * covered twice.  *first_bad (host) gets -1 when all is well, else the flat
+ * covered twice (sequences that share blocks through prefix sharing alias
+ * by design: check them one at a time).  *first_bad (host) gets -1 when all
+ * is well, else the flat
  * index b*max_blocks_per_seq + j of the first bad entry (status
  * PKV_ERR_BAD_TABLE); a seq_len below 0 or beyond max_blocks_per_seq*16 is
  * reported at index b*max_blocks_per_seq. */

@@ -71,12 +71,26 @@ class OutOfBlocks(RuntimeError):
     pass
 
 
+class SharedBlock(RuntimeError):
+    """A growth would write into a partly filled block another table holds."""
+
+
 class Allocator:
     """Free list of physical blocks handed out on demand.
 
     Blocks leave the free list from the front, in the given order; released
     blocks return to the back in table order.  A sequence's table grows by one
-    block exactly when a token opens a new logical block."""
+    block exactly when a token opens a new logical block.
+
+    Prefix sharing [P2 section 3.1: shared-prefix blocks are reused, with
+    copy-on-write; P1 section 5: prefix cache]: each block counts the tables
+    that hold it and is free again only when none does.  fork() gives a new
+    sequence every block of another; publish_prefix() / match_prefix() let a
+    new sequence take over the full blocks of an earlier one whose prefix
+    hashes (computed by the caller) agree.  A growth that writes into a partly
+    filled last block held by another table is refused by reserve(); with
+    reserve_cow() the sequence first moves onto a fresh block (taken before the
+    growth's own blocks) and the (shared, fresh) pair to copy is returned."""
 
     def __init__(self, num_blocks: int, free_order=None, block_size: int = BLOCK):
         order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
@@ -86,26 +100,96 @@ class Allocator:
         self.free = list(order)
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
+        self.refs = [0] * num_blocks
+        self.by_hash: dict[int, int] = {}
+        self.hash_of: dict[int, int] = {}
 
-    def reserve(self, seq: int, new_len: int) -> list[int]:
+    def _grow(self, seq, new_len, cow):
         table = list(self.tables.get(seq, []))
         old_len = self.lens.get(seq, 0)
         if new_len < old_len:
             raise ValueError("a sequence never shrinks")
         free = list(self.free)
+        refs = list(self.refs)
+        pair = None
+        writes_tail = new_len > old_len and old_len % self.block_size != 0
+        if writes_tail and refs[table[-1]] > 1:
+            if not cow:
+                raise SharedBlock(f"sequence {seq} would write into shared block {table[-1]}")
+            if not free:
+                raise OutOfBlocks(f"no free block to copy block {table[-1]} into")
+            fresh = free.pop(0)
+            refs[fresh] = 1
+            refs[table[-1]] -= 1
+            pair = (table[-1], fresh)
+            table[-1] = fresh
         for t in range(old_len, new_len):
             block_id = t // self.block_size
             if block_id == len(table):           # token t opens a new logical block
                 if not free:                     # all-or-nothing: nothing changes
                     raise OutOfBlocks(f"no free block for sequence {seq} token {t}")
-                table.append(free.pop(0))
-        self.free = free
+                b = free.pop(0)
+                refs[b] = 1
+                table.append(b)
+        self.free, self.refs = free, refs
         self.tables[seq] = table
         self.lens[seq] = new_len
-        return list(table)
+        return list(table), pair
+
+    def reserve(self, seq: int, new_len: int) -> list[int]:
+        return self._grow(seq, new_len, cow=False)[0]
+
+    def reserve_cow(self, seq: int, new_len: int):
+        """(table, (shared block, fresh block) to copy, or None)."""
+        return self._grow(seq, new_len, cow=True)
+
+    def fork(self, src: int, dst: int) -> None:
+        if src == dst or src not in self.tables or dst in self.tables:
+            raise ValueError("fork needs an existing source and a new destination")
+        self.tables[dst] = list(self.tables[src])
+        self.lens[dst] = self.lens[src]
+        for b in self.tables[dst]:
+            self.refs[b] += 1
+
+    def publish_prefix(self, seq: int, block_hashes) -> None:
+        if seq not in self.tables:
+            if len(block_hashes):
+                raise ValueError("unknown sequence")
+            return
+        if len(block_hashes) * self.block_size > self.lens[seq]:
+            raise ValueError("only full blocks can be published")
+        for j, h in enumerate(block_hashes):
+            b = self.tables[seq][j]
+            if int(h) in self.by_hash or b in self.hash_of:
+                continue                          # the first entry stays
+            self.by_hash[int(h)] = b
+            self.hash_of[b] = int(h)
+
+    def match_prefix(self, seq: int, block_hashes) -> int:
+        if seq in self.tables and (self.lens[seq] or self.tables[seq]):
+            raise ValueError("prefix matching needs a new sequence")
+        table = []
+        for h in block_hashes:
+            b = self.by_hash.get(int(h))
+            if b is None:
+                break
+            self.refs[b] += 1
+            table.append(b)
+        self.tables[seq] = table
+        self.lens[seq] = len(table) * self.block_size
+        return len(table)
+
+    def refcount(self, block: int) -> int:
+        return self.refs[block]
 
     def release(self, seq: int) -> None:
-        self.free.extend(self.tables.pop(seq, []))
+        for b in self.tables.pop(seq, []):
+            self.refs[b] -= 1
+            if self.refs[b] == 0:
+                h = self.hash_of.pop(b, None)
+                if h is not None:
+                    del self.by_hash[h]
+                self.free.append(b)
         self.lens.pop(seq, None)
 
     def waste_slots(self, seq: int) -> int:
@@ -307,6 +391,22 @@ def append_sequence(cache: Cache, k_seq, v_seq, table_row, pos0: int = 0, heads=
                 cache.v[blk, h, :, off:off + cnt] = vx[i:i + cnt].T
                 i += cnt
     return cache
+
+
+def copy_blocks(src: Cache, dst: Cache, src_ids, dst_ids) -> Cache:
+    """Block dst_ids[i] of dst takes every page of block src_ids[i] of src (and
+    its E4M3 scales): the copy of copy-on-write [P2 section 3.1] and of moving
+    blocks between memory tiers [P1 section 4].  Pairs naming a block outside
+    its pool are skipped.  Pages are copied whole, whatever their inner order."""
+    for sb, db in zip(np.asarray(src_ids).tolist(), np.asarray(dst_ids).tolist()):
+        if not (0 <= sb < src.num_blocks and 0 <= db < dst.num_blocks):
+            continue
+        dst.k[db] = src.k[sb]
+        dst.v[db] = src.v[sb]
+        if src.fmt == "e4m3":
+            dst.k_scale[db] = src.k_scale[sb]
+            dst.v_scale[db] = src.v_scale[sb]
+    return dst
 
 
 # --------------------------------------------------------------------------

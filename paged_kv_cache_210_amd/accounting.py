@@ -12,6 +12,14 @@ SCALE_GROUP = 64
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor spec
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor spec
+PCIE_PEAK_GBS = 64.0            # PCIe 5.0 x16 host link, per direction (32 GT/s x 16 lanes)
+
+
+def block_bytes(hkv, head_dim, kv_dtype):
+    """K + V bytes of one physical block (all kv heads), plus its two fp32
+    scales per kv head for E4M3 pools: what pkv_copy_blocks moves per block."""
+    b = 2 * hkv * 16 * head_dim * ELEM_BYTES[kv_dtype]
+    return b + (2 * hkv * 4 if kv_dtype == "e4m3" else 0)
 
 
 def kv_cache_bytes(layers, kv_heads, head_dim, tokens=1, elem_bytes=2):

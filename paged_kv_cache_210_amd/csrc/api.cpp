@@ -67,6 +67,7 @@ extern "C" const char* pkv_status_str(int32_t status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_DEVICE: return "HIP runtime error";
     case PKV_ERR_BAD_TABLE: return "block table entry out of range or aliased";
+    case PKV_ERR_SHARED: return "write into a block shared with another sequence";
     default: return "unknown status";
   }
 }
@@ -257,6 +258,56 @@ extern "C" int32_t pkv_attn_lse_merge(int32_t S, int64_t rows, int32_t head_dim,
   a.out_l = out_l;
   a.out_lse = out_lse;
   return from_hip(pkv::launch_merge(a, stream_of(stream)));
+}
+
+// Memory a kernel may address: device memory, or host memory pinned and
+// mapped for the device.  Pageable host memory is refused before any launch.
+bool device_addressable(const void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();          // do not leave the failed query as a sticky error
+    return false;
+  }
+  return at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeHost ||
+         at.type == hipMemoryTypeManaged || at.type == hipMemoryTypeUnified;
+}
+
+extern "C" int32_t pkv_copy_blocks(const pkv_cache_desc* src, const pkv_cache_desc* dst,
+                                   const int32_t* src_ids, const int32_t* dst_ids, int32_t n,
+                                   void* stream) {
+  int32_t st = check_cache(src);
+  if (st != PKV_OK) return st;
+  st = check_cache(dst);
+  if (st != PKV_OK) return st;
+  if (src->kv_dtype != dst->kv_dtype || src->num_kv_heads != dst->num_kv_heads ||
+      src->head_dim != dst->head_dim || n < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  if (!src_ids || !dst_ids) return PKV_ERR_INVALID_ARG;
+  const bool f8 = src->kv_dtype == PKV_FP8_E4M3;
+  const void* need[] = {src->k_cache, src->v_cache, dst->k_cache, dst->v_cache, src_ids, dst_ids,
+                        src->k_scale, src->v_scale, dst->k_scale, dst->v_scale};
+  for (int i = 0; i < (f8 ? 10 : 6); ++i)
+    if (!device_addressable(need[i])) return PKV_ERR_INVALID_ARG;
+  const int es = elem_size(src->kv_dtype);
+  pkv::CopyArgs a{};
+  a.src_k = static_cast<const uint8_t*>(src->k_cache);
+  a.src_v = static_cast<const uint8_t*>(src->v_cache);
+  a.dst_k = static_cast<uint8_t*>(dst->k_cache);
+  a.dst_v = static_cast<uint8_t*>(dst->v_cache);
+  a.src_stride = src->block_stride * es;
+  a.dst_stride = dst->block_stride * es;
+  a.region = (int64_t)src->num_kv_heads * PKV_BLOCK_SIZE * src->head_dim * es;
+  a.src_ks = f8 ? src->k_scale : nullptr;
+  a.src_vs = f8 ? src->v_scale : nullptr;
+  a.dst_ks = f8 ? dst->k_scale : nullptr;
+  a.dst_vs = f8 ? dst->v_scale : nullptr;
+  a.hkv = src->num_kv_heads;
+  a.src_blocks = src->num_blocks;
+  a.dst_blocks = dst->num_blocks;
+  a.src_ids = src_ids;
+  a.dst_ids = dst_ids;
+  return from_hip(pkv::launch_copy_blocks(a, n, stream_of(stream)));
 }
 
 extern "C" int32_t pkv_validate_tables(const int32_t* block_tables, const int32_t* seq_lens,

@@ -1,0 +1,58 @@
+// Whole-block copies between block pools.
+//
+// [P2] "Unlocking long context ..." section 3.1: blocks of a shared prefix are
+// reused with copy-on-write, so a sequence about to write into a shared, partly
+// filled block first gets a private copy of it (the allocator names the pair).
+// [P1] "Long-context inference engineering truths 2026 ..." section 4: KV
+// blocks not needed for a while move from HBM to host memory and back.  Both
+// are the same operation: copy every kv head's K and V page (and, for E4M3
+// pools, the two scales) of block src_ids[i] of one pool to block dst_ids[i]
+// of another.  A pool in pinned host memory is addressed by the kernel
+// directly (its loads or stores cross PCIe), so an offload or a page-in is one
+// launch on the caller's stream, which can overlap attention on another.
+#include <algorithm>
+
+#include "pkv_common.h"
+
+namespace pkv {
+namespace {
+
+constexpr int CT = 256;
+
+// One workgroup copies a 1/gridDim.y share of one block pair with 16-byte
+// loads and stores; K and V regions of a block are contiguous runs of
+// `region` bytes in their pools.
+__global__ __launch_bounds__(CT) void copy_blocks_kernel(CopyArgs a) {
+  const int i = blockIdx.x;
+  const int sb = a.src_ids[i], db = a.dst_ids[i];
+  if ((unsigned)sb >= (unsigned)a.src_blocks || (unsigned)db >= (unsigned)a.dst_blocks) return;
+  const u32x4* sk = reinterpret_cast<const u32x4*>(a.src_k + sb * a.src_stride);
+  const u32x4* sv = reinterpret_cast<const u32x4*>(a.src_v + sb * a.src_stride);
+  u32x4* dk = reinterpret_cast<u32x4*>(a.dst_k + db * a.dst_stride);
+  u32x4* dv = reinterpret_cast<u32x4*>(a.dst_v + db * a.dst_stride);
+  const int64_t n16 = a.region >> 4;
+  for (int64_t o = (int64_t)blockIdx.y * CT + threadIdx.x; o < n16; o += (int64_t)CT * gridDim.y) {
+    const u32x4 k = sk[o];
+    const u32x4 v = sv[o];
+    dk[o] = k;
+    dv[o] = v;
+  }
+  if (a.src_ks && blockIdx.y == 0 && (int)threadIdx.x < a.hkv) {
+    const int h = threadIdx.x;
+    a.dst_ks[(int64_t)db * a.hkv + h] = a.src_ks[(int64_t)sb * a.hkv + h];
+    a.dst_vs[(int64_t)db * a.hkv + h] = a.src_vs[(int64_t)sb * a.hkv + h];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t per_block = (a.region >> 4) / CT;            // full passes of one workgroup
+  // few pairs (a copy-on-write): split each block over several workgroups
+  int split = (int)std::max<int64_t>(1, std::min<int64_t>(per_block, (512 + n - 1) / n));
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, split), dim3(CT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -135,6 +135,26 @@ hipError_t launch_prefill(const CacheView& c, const void* q, int T, int hq, int 
                           float scale, void* out, float* out_lse, float* part_o, float* part_m,
                           float* part_l, hipStream_t s);
 
+// Whole-block copies (copy-on-write, offload): K/V regions of `region` bytes
+// per block, block strides in bytes; scales copied when src_ks is set.
+struct CopyArgs {
+  const uint8_t* src_k;
+  const uint8_t* src_v;
+  uint8_t* dst_k;
+  uint8_t* dst_v;
+  int64_t src_stride, dst_stride;
+  int64_t region;
+  const float* src_ks;
+  const float* src_vs;
+  float* dst_ks;
+  float* dst_vs;
+  int hkv;
+  int src_blocks, dst_blocks;
+  const int32_t* src_ids;
+  const int32_t* dst_ids;
+};
+hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t s);
+
 // Generic strided merge of S partial states per row.
 struct MergeArgs {
   int S;

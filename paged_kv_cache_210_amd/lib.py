@@ -22,6 +22,7 @@ PKV_ERR_NO_BLOCKS = -3
 PKV_ERR_WORKSPACE = -4
 PKV_ERR_DEVICE = -5
 PKV_ERR_BAD_TABLE = -6
+PKV_ERR_SHARED = -7
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 BLOCK_SIZE = 16
@@ -56,6 +57,16 @@ _SIGS = {
     "pkv_allocator_waste_slots": (c_int32, [c_void_p, c_int32, POINTER(c_int64)]),
     "pkv_allocator_free_count": (c_int32, [c_void_p, POINTER(c_int32)]),
     "pkv_allocator_destroy": (None, [c_void_p]),
+    "pkv_allocator_reserve_cow": (c_int32, [c_void_p, c_int32, c_int64, c_void_p, c_int32,
+                                            POINTER(c_int32), POINTER(c_int32),
+                                            POINTER(c_int32)]),
+    "pkv_allocator_fork": (c_int32, [c_void_p, c_int32, c_int32]),
+    "pkv_allocator_publish_prefix": (c_int32, [c_void_p, c_int32, c_void_p, c_int32]),
+    "pkv_allocator_match_prefix": (c_int32, [c_void_p, c_int32, c_void_p, c_int32,
+                                             POINTER(c_int32)]),
+    "pkv_allocator_refcount": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
+    "pkv_copy_blocks": (c_int32, [POINTER(CacheDesc), POINTER(CacheDesc), c_void_p, c_void_p,
+                                  c_int32, c_void_p]),
     "pkv_kv_append": (c_int32, [POINTER(CacheDesc), c_void_p, c_void_p, c_int32, c_int32,
                                 c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
     "pkv_fp8_group_scales": (c_int32, [POINTER(CacheDesc), c_void_p, c_void_p, c_int32, c_int32,
@@ -144,18 +155,21 @@ class PagedCache:
         self.device = k.device
 
     @classmethod
-    def empty(cls, num_blocks, hkv, head_dim, kv_dtype, device="cuda", fill=None):
+    def empty(cls, num_blocks, hkv, head_dim, kv_dtype, device="cuda", fill=None, pinned=False):
+        """A pool on `device`; pinned=True puts it in pinned host memory instead
+        (device-addressable: the target or source of an offload)."""
         code = KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else kv_dtype
         dt = _CODE_DTYPE[code]
-        k = torch.empty(num_blocks, hkv, BLOCK_SIZE, head_dim, dtype=dt, device=device)
-        v = torch.empty(num_blocks, hkv, head_dim, BLOCK_SIZE, dtype=dt, device=device)
+        kw = dict(device="cpu", pin_memory=True) if pinned else dict(device=device)
+        k = torch.empty(num_blocks, hkv, BLOCK_SIZE, head_dim, dtype=dt, **kw)
+        v = torch.empty(num_blocks, hkv, head_dim, BLOCK_SIZE, dtype=dt, **kw)
         if fill is not None:
             k.fill_(fill)
             v.fill_(fill)
         ks = vs = None
         if code == PKV_FP8_E4M3:
-            ks = torch.ones(num_blocks, hkv, dtype=torch.float32, device=device)
-            vs = torch.ones(num_blocks, hkv, dtype=torch.float32, device=device)
+            ks = torch.ones(num_blocks, hkv, dtype=torch.float32, **kw)
+            vs = torch.ones(num_blocks, hkv, dtype=torch.float32, **kw)
         return cls(k, v, code, ks, vs)
 
     def desc(self) -> CacheDesc:
@@ -186,6 +200,38 @@ class Allocator:
         _check(load().pkv_allocator_reserve(self._h, seq, new_len, row, max_blocks,
                                             ctypes.byref(n)), "allocator_reserve")
         return list(row[:n.value])
+
+    def reserve_cow(self, seq: int, new_len: int, max_blocks: int = None):
+        """reserve() that may first move the sequence off a shared last block;
+        returns (table, (src, dst) of the block copy to make, or None)."""
+        max_blocks = max_blocks or max(1, -(-new_len // BLOCK_SIZE))
+        row = (c_int32 * max_blocks)()
+        n, cs, cd = c_int32(), c_int32(), c_int32()
+        _check(load().pkv_allocator_reserve_cow(self._h, seq, new_len, row, max_blocks,
+                                                ctypes.byref(n), ctypes.byref(cs),
+                                                ctypes.byref(cd)), "allocator_reserve_cow")
+        return list(row[:n.value]), (None if cs.value < 0 else (cs.value, cd.value))
+
+    def fork(self, src_seq: int, dst_seq: int):
+        _check(load().pkv_allocator_fork(self._h, src_seq, dst_seq), "allocator_fork")
+
+    def publish_prefix(self, seq: int, block_hashes):
+        arr = (ctypes.c_uint64 * max(1, len(block_hashes)))(*[int(h) for h in block_hashes])
+        _check(load().pkv_allocator_publish_prefix(self._h, seq, arr, len(block_hashes)),
+               "allocator_publish_prefix")
+
+    def match_prefix(self, seq: int, block_hashes) -> int:
+        arr = (ctypes.c_uint64 * max(1, len(block_hashes)))(*[int(h) for h in block_hashes])
+        out = c_int32()
+        _check(load().pkv_allocator_match_prefix(self._h, seq, arr, len(block_hashes),
+                                                 ctypes.byref(out)), "allocator_match_prefix")
+        return out.value
+
+    def refcount(self, block: int) -> int:
+        out = c_int32()
+        _check(load().pkv_allocator_refcount(self._h, block, ctypes.byref(out)),
+               "allocator_refcount")
+        return out.value
 
     def release(self, seq: int):
         _check(load().pkv_allocator_release(self._h, seq), "allocator_release")
@@ -392,6 +438,20 @@ def attn_lse_merge(part_o, part_m, part_l, out_dtype=torch.bfloat16, out=None, w
                                      _DTYPE_CODE[out.dtype], _p(m), _p(l), _p(lse), _stream(dev)),
            "attn_lse_merge")
     return out, m, l, lse
+
+
+def copy_blocks(src: PagedCache, dst: PagedCache, src_ids, dst_ids, stream=None):
+    """pkv_copy_blocks: block src_ids[i] of src -> block dst_ids[i] of dst
+    (int32 id tensors on the GPU).  `stream` is a torch.cuda.Stream or None
+    for the current stream of the ids' device."""
+    _need(src_ids, torch.int32, "src_ids")
+    _need(dst_ids, torch.int32, "dst_ids", src_ids.device, tuple(src_ids.shape))
+    if not src_ids.is_cuda:
+        raise ValueError("src_ids / dst_ids must be on the GPU")
+    s = c_void_p(stream.cuda_stream) if stream is not None else _stream(src_ids.device)
+    ds, dd = src.desc(), dst.desc()
+    _check(load().pkv_copy_blocks(ctypes.byref(ds), ctypes.byref(dd), _p(src_ids), _p(dst_ids),
+                                  src_ids.numel(), s), "copy_blocks")
 
 
 def validate_tables(block_tables, seq_lens, num_blocks):

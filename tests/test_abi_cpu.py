@@ -150,3 +150,85 @@ def test_entry_point_argument_checks(lib):
                                 None, None, None) == lib.PKV_ERR_INVALID_ARG
     assert L.pkv_attn_lse_merge(2, 4, 128, 0x1000, 0x2000, 0x3000, 0x4000, lib.PKV_FP8_E4M3, None,
                                 None, None, None) == lib.PKV_ERR_UNSUPPORTED
+
+
+def test_sharing_allocator_matches_oracle_step_for_step(lib):
+    """Fork, copy-on-write growth, prefix publish / match and release through
+    the C ABI, against the oracle allocator: same tables, copy pairs,
+    reference counts, free counts and refusals."""
+    nb = 40
+    order = synth.free_order(nb, 78).numpy()
+    a = lib.Allocator(nb, order)
+    o = O.Allocator(nb, order)
+    r = np.random.default_rng(2)
+    for step in range(1200):
+        op = r.random()
+        s = int(r.integers(0, 6))
+        if op < 0.4:
+            n = o.lens.get(s, 0) + int(r.integers(0, 30))
+            cow = r.random() < 0.7
+            try:
+                want = o.reserve_cow(s, n) if cow else (o.reserve(s, n), None)
+            except (O.OutOfBlocks, O.SharedBlock) as ex:
+                code = lib.PKV_ERR_NO_BLOCKS if isinstance(ex, O.OutOfBlocks) else lib.PKV_ERR_SHARED
+                with pytest.raises(lib.PkvError) as e:
+                    a.reserve_cow(s, n, max_blocks=nb) if cow else a.reserve(s, n, max_blocks=nb)
+                assert e.value.status == code
+            else:
+                got = a.reserve_cow(s, n, max_blocks=nb) if cow else (a.reserve(s, n, max_blocks=nb), None)
+                assert got == want
+        elif op < 0.55:
+            d = int(r.integers(0, 6))
+            try:
+                o.fork(s, d)
+            except ValueError:
+                with pytest.raises(lib.PkvError) as e:
+                    a.fork(s, d)
+                assert e.value.status == lib.PKV_ERR_INVALID_ARG
+            else:
+                a.fork(s, d)
+        elif op < 0.7:
+            full = o.lens.get(s, 0) // 16
+            hs = [int(x) for x in r.integers(0, 6, size=full + int(r.integers(0, 2)))]
+            try:
+                o.publish_prefix(s, hs)
+            except ValueError:
+                with pytest.raises(lib.PkvError):
+                    a.publish_prefix(s, hs)
+            else:
+                a.publish_prefix(s, hs)
+        elif op < 0.82:
+            hs = [int(x) for x in r.integers(0, 6, size=int(r.integers(0, 4)))]
+            try:
+                m = o.match_prefix(s, hs)
+            except ValueError:
+                with pytest.raises(lib.PkvError):
+                    a.match_prefix(s, hs)
+            else:
+                assert a.match_prefix(s, hs) == m
+        else:
+            a.release(s)
+            o.release(s)
+        assert a.free_count() == o.free_count()
+        for b in range(nb):
+            assert a.refcount(b) == o.refcount(b), (step, b)
+        for q in range(6):
+            assert a.waste_slots(q) == o.waste_slots(q)
+    a.close()
+
+
+def test_copy_blocks_argument_checks(lib):
+    """Refusals that happen before any device query or launch."""
+    L = lib.load()
+    ids = ctypes.c_void_p(0x1000)
+    bf = _desc(lib)
+    for other, n in ((_desc(lib, num_kv_heads=4, block_stride=4 * 16 * 128), 1),
+                     (_desc(lib, head_dim=64, block_stride=8 * 16 * 64), 1),
+                     (_desc(lib, kv_dtype=lib.PKV_F32), 1),
+                     (_desc(lib), -1)):
+        assert L.pkv_copy_blocks(ctypes.byref(bf), ctypes.byref(other), ids, ids, n, None) == \
+            lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_copy_blocks(ctypes.byref(bf), ctypes.byref(bf), ids, ids, 0, None) == lib.PKV_OK
+    assert L.pkv_copy_blocks(ctypes.byref(bf), ctypes.byref(bf), None, ids, 3, None) == \
+        lib.PKV_ERR_INVALID_ARG
+    assert lib.status_str(lib.PKV_ERR_SHARED).startswith("write into a block shared")

@@ -468,3 +468,145 @@ def test_bulk_append_equals_token_append(fmt):
     O.append_sequence(c, kk, vv, tables[0], 0, heads=[1])
     np.testing.assert_array_equal(c.k[:, 1], a.k[:, 1])
     assert not c.k[:, 0].any()
+
+
+# ---------------------------------------------------------------- prefix sharing
+def _chain_hashes(tokens):
+    """Caller-side prefix hashes: hash j covers tokens [0, 16(j+1))."""
+    out, h = [], 1469598103934665603
+    for j in range(len(tokens) // 16):
+        for t in tokens[16 * j:16 * j + 16]:
+            h = ((h ^ int(t)) * 1099511628211) % (1 << 64)
+        out.append(h)
+    return out
+
+
+def _check_sharing_state(alloc, nb):
+    held = {}
+    for s, t in alloc.tables.items():
+        for b in t:
+            held[b] = held.get(b, 0) + 1
+    for b in range(nb):
+        assert alloc.refcount(b) == held.get(b, 0)
+    assert not set(held) & set(alloc.free)
+    assert len(held) + alloc.free_count() == nb
+    assert len(set(alloc.free)) == len(alloc.free)
+    for h, b in alloc.by_hash.items():
+        assert alloc.hash_of[b] == h and b in held
+
+
+def test_sharing_allocator_keeps_every_sequence_its_own_tokens():
+    """Brute force against the plain definition: every sequence owns its list
+    of token values.  Tokens are written through the table into an oracle pool
+    (K = the token value), shared blocks are copied with copy_blocks when
+    reserve_cow names a pair, sequences fork and take over published prefixes,
+    and after every step each sequence reads back exactly its own tokens."""
+    nb = 48
+    alloc = O.Allocator(nb, synth.free_order(nb, 99).numpy())
+    cache = O.new_cache(nb, 1, 4, "f32", fill=np.nan)
+    truth = {}
+    r = np.random.default_rng(5)
+    next_val = [1.0]
+
+    def write(seq, n_new):
+        toks = []
+        for _ in range(n_new):
+            toks.append(next_val[0])
+            next_val[0] += 1.0
+        return toks
+
+    for step in range(1500):
+        op = r.random()
+        seqs = sorted(truth)
+        if op < 0.45 or not seqs:                       # grow a sequence
+            s = int(r.integers(0, 8))
+            old = truth.get(s, [])
+            toks = write(s, int(r.integers(1, 24)))
+            try:
+                table, pair = alloc.reserve_cow(s, len(old) + len(toks))
+            except O.OutOfBlocks:
+                continue
+            if pair is not None:
+                O.copy_blocks(cache, cache, [pair[0]], [pair[1]])
+            tab = np.array([table], dtype=np.int32)
+            vals = np.array(toks, dtype=np.float32)[:, None, None] * np.ones((1, 1, 4), np.float32)
+            O.append(cache, vals, vals, np.zeros(len(toks), np.int32),
+                     np.arange(len(old), len(old) + len(toks)), tab)
+            truth[s] = old + toks
+        elif op < 0.6:                                  # fork
+            s = seqs[int(r.integers(0, len(seqs)))]
+            d = int(r.integers(0, 8))
+            if d in truth:
+                continue
+            alloc.fork(s, d)
+            truth[d] = list(truth[s])
+        elif op < 0.72:                                 # publish full blocks
+            s = seqs[int(r.integers(0, len(seqs)))]
+            hs = _chain_hashes(truth[s])
+            alloc.publish_prefix(s, hs)
+        elif op < 0.82:                                 # a new sequence reuses a prefix
+            s = seqs[int(r.integers(0, len(seqs)))]
+            d = int(r.integers(0, 8))
+            if d in truth:
+                continue
+            extra = write(d, 5)
+            want = _chain_hashes(truth[s]) + _chain_hashes(truth[s] + extra)[len(truth[s]) // 16:]
+            m = alloc.match_prefix(d, want)
+            published = [h for h in want if h in alloc.by_hash]
+            assert m <= len(want)
+            truth[d] = truth[s][:16 * m]
+            assert m == 0 or alloc.tables[d] == [alloc.by_hash[h] for h in want[:m]]
+            assert set(want[:m]) <= set(published)
+        else:                                           # release
+            s = seqs[int(r.integers(0, len(seqs)))]
+            alloc.release(s)
+            del truth[s]
+        _check_sharing_state(alloc, nb)
+        for s, toks in truth.items():
+            assert alloc.lens[s] == len(toks)
+            if toks:
+                K, _ = O.gather_kv(cache, alloc.tables[s], len(toks), 0)
+                assert np.array_equal(K[:, 0], np.array(toks)), (step, s)
+
+
+def test_plain_reserve_refuses_to_write_into_a_shared_block():
+    alloc = O.Allocator(8)
+    alloc.reserve(0, 20)                         # blocks 0, 1 (block 1 partly filled)
+    alloc.fork(0, 1)
+    assert alloc.refcount(1) == 2
+    with pytest.raises(O.SharedBlock):
+        alloc.reserve(0, 21)
+    assert alloc.lens[0] == 20 and alloc.free_count() == 6
+    table, pair = alloc.reserve_cow(1, 40)       # fresh block first, then growth
+    assert pair == (1, 2) and table == [0, 2, 3]
+    assert alloc.refcount(1) == 1 and alloc.refcount(0) == 2
+    assert alloc.reserve(0, 32) == [0, 1]        # sole holder now: writes in place
+    alloc2 = O.Allocator(4)
+    alloc2.reserve(0, 32)                        # full last block: growth never copies
+    alloc2.fork(0, 1)
+    assert alloc2.reserve_cow(1, 33) == ([0, 1, 2], None)
+    alloc3 = O.Allocator(2)
+    alloc3.reserve(0, 20)
+    alloc3.fork(0, 1)
+    with pytest.raises(O.OutOfBlocks):           # no block left for the copy
+        alloc3.reserve_cow(1, 21)
+    assert alloc3.tables[1] == [0, 1] and alloc3.refcount(1) == 2
+
+
+def test_published_prefix_leaves_index_when_freed():
+    alloc = O.Allocator(8)
+    toks = list(range(40))
+    alloc.reserve(0, 40)
+    hs = _chain_hashes(toks)
+    with pytest.raises(ValueError):              # the third block is not full
+        alloc.publish_prefix(0, hs + [123])
+    alloc.publish_prefix(0, hs)
+    assert alloc.match_prefix(5, hs) == 2 and alloc.lens[5] == 32
+    assert alloc.tables[5] == alloc.tables[0][:2]
+    assert alloc.match_prefix(6, [hs[0], 999, hs[1]]) == 1
+    alloc.release(0)
+    alloc.release(5)
+    assert alloc.by_hash and alloc.refcount(alloc.tables[6][0]) == 1
+    alloc.release(6)
+    assert not alloc.by_hash and alloc.free_count() == 8
+    assert alloc.match_prefix(7, hs) == 0
