@@ -79,18 +79,23 @@ def _decode_setup(cfg, partition_blocks):
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
     del inp, keep
     torch.cuda.synchronize()
+    # the folded step needs a bf16 pool and at most 16 query heads per kv head
+    folded = cfg.kv_dtype == "bf16" and cfg.q_dtype == "bf16" and cfg.hq // cfg.hkv <= 16
     return dict(cache=cache, caches=(cache, twin), td=td, q=q, lens=lens, part=part, out=out,
-                lse=lse, step_in=step_in, tables=tables, partitions=P)
+                lse=lse, step_in=step_in, tables=tables, partitions=P, folded=folded)
 
 
 def bench_decode(cfg, steps, warmup, partition_blocks=0):
     """Returns (ms per step, ms per split-KV decode kernel, ms per merge, state).
 
-    A step is pkv_kv_append + pkv_paged_attn_decode_partial + pkv_attn_lse_merge,
-    the two launches pkv_paged_attn_decode makes, with events between them so
-    the dominant kernel is timed on its own.  Steps alternate between two pools
-    holding the same KV, so no step reads pages still cached from the one
-    before."""
+    A step appends the newest token of every sequence and attends with it:
+    for bf16 pools pkv_paged_attn_decode_step_partial (the append folded into
+    the decode launch) + pkv_attn_lse_merge, the launches of
+    pkv_paged_attn_decode_step; for E4M3 pools pkv_kv_append +
+    pkv_paged_attn_decode_partial + pkv_attn_lse_merge.  Events sit between
+    the launches so the dominant kernel is timed on its own.  Steps alternate
+    between two pools holding the same KV, so no step reads pages still
+    cached from the one before."""
     import torch
     from paged_kv_cache_210_amd import lib
 
@@ -102,11 +107,18 @@ def bench_decode(cfg, steps, warmup, partition_blocks=0):
     def step(ev=None):
         cache = st["caches"][it[0] % 2]
         it[0] += 1
-        lib.kv_append(cache, s["k"], s["v"], s["seq"], s["pos"], st["td"])
-        if ev is not None:
-            ev[0].record()
-        lib.paged_attn_decode_partial(cache, st["q"], st["td"], st["lens"],
-                                      partition_blocks=partition_blocks, part=st["part"])
+        if st["folded"]:
+            if ev is not None:
+                ev[0].record()
+            lib.paged_attn_decode_step(cache, s["k"], s["v"], st["q"], st["td"], st["lens"],
+                                       partition_blocks=partition_blocks, partial=True,
+                                       part=st["part"])
+        else:
+            lib.kv_append(cache, s["k"], s["v"], s["seq"], s["pos"], st["td"])
+            if ev is not None:
+                ev[0].record()
+            lib.paged_attn_decode_partial(cache, st["q"], st["td"], st["lens"],
+                                          partition_blocks=partition_blocks, part=st["part"])
         if ev is not None:
             ev[1].record()
         lib.attn_lse_merge(po, pm, pl, out=st["out"], with_state=False, out_lse=st["lse"])
@@ -140,6 +152,8 @@ def decode_record(cfg, steps, warmup, partition_blocks):
                                    cfg.kv_dtype)
     step_bytes = A.decode_step_bytes(cfg.seq_lens, cfg.hq, cfg.hkv, cfg.head_dim, cfg.q_dtype,
                                      cfg.kv_dtype)
+    if st["folded"]:       # the folded append reads the new K/V and writes it into the pool
+        kbytes += A.append_bytes(cfg.batch, cfg.hkv, cfg.head_dim, cfg.kv_dtype) - 8 * cfg.batch
     gbs = kbytes / (ms_dec * 1e-3) / 1e9
     rec = {
         "workload": cfg.name,
@@ -150,7 +164,9 @@ def decode_record(cfg, steps, warmup, partition_blocks):
         "partitions": st["partitions"],
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / A.HBM_PEAK_GBS, "traffic": measured_traffic(cfg),
-                     "kernel": "decode_mfma_kernel (pkv_paged_attn_decode_partial)",
+                     "kernel": ("decode_mfma_kernel with the append folded in "
+                                "(pkv_paged_attn_decode_step_partial)" if st["folded"] else
+                                "decode_mfma_kernel (pkv_paged_attn_decode_partial)"),
                      "ms_per_launch": ms_dec, "ms_per_launch_median": st["decode_ms_median"],
                      "ms_per_launch_min": st["decode_ms_min"], "bytes_per_launch": kbytes},
     }
@@ -574,7 +590,7 @@ def main(argv=None):
         "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_lens[0],
                    "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
                    "block_size": 16, "kv_dtype": cfg.kv_dtype, "pool_blocks": cfg.pool_blocks,
-                   "step": "kv_append(1 token/seq) + split-KV decode + LSE merge"},
+                   "step": "append 1 token/seq folded into split-KV decode (pkv_paged_attn_decode_step) + LSE merge"},
         "decode_hbm_gbs": head["roofline"]["achieved"],
         "hbm_copy_gbs": copy["gbs"],
         "roofline": head["roofline"],

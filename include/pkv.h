@@ -257,6 +257,33 @@ int32_t pkv_paged_attn_decode_partial(const pkv_cache_desc* cache, const void* q
                                       int32_t partition_blocks, float* part_o, float* part_m,
                                       float* part_l, void* stream);
 
+/* ---- decode step with the append folded in [P1 2.2, P2 5.1] ----------------
+ * pkv_kv_append of one token per sequence followed by pkv_paged_attn_decode
+ * (or its partial form), in the launches of the decode alone: token
+ * seq_lens[b] - 1 of sequence b takes k_new[b][h][:] and v_new[b][h][:]
+ * (device bf16 [B][num_kv_heads][head_dim], 16-byte aligned), which the
+ * kernel uses directly and writes into its pool slot, so seq_lens already
+ * count the new token.  The pool ends bit for bit as after pkv_kv_append, and
+ * the outputs equal those of the two calls.  Sequences with seq_lens[b] == 0
+ * (or beyond the table) append nothing; a block id outside the pool skips the
+ * token (as pkv_kv_append does).  bf16 q and bf16 cache only, with at most 16
+ * query heads per kv head (otherwise PKV_ERR_UNSUPPORTED: make the two calls).
+ * Other arguments, workspace and outputs as pkv_paged_attn_decode /
+ * pkv_paged_attn_decode_partial. */
+int32_t pkv_paged_attn_decode_step(const pkv_cache_desc* cache, const void* k_new,
+                                   const void* v_new, const void* q, int32_t q_dtype, int32_t B,
+                                   int32_t num_q_heads, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   float scale, int32_t partition_blocks, void* out,
+                                   float* out_lse, void* ws, size_t ws_bytes, void* stream);
+int32_t pkv_paged_attn_decode_step_partial(const pkv_cache_desc* cache, const void* k_new,
+                                           const void* v_new, const void* q, int32_t q_dtype,
+                                           int32_t B, int32_t num_q_heads,
+                                           const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                           float scale, int32_t partition_blocks, float* part_o,
+                                           float* part_m, float* part_l, void* stream);
+
 /* ---- chunked causal prefill against paged KV [P2 4.1, P2 5.2, P3 1.2] ----
  * Query rows q[r] (r < T) of one sequence sit at absolute positions q_pos0+r.
  * Row r attends to keys t with kv_begin <= t < kv_end and, when causal, t <=

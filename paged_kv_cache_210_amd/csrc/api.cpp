@@ -201,6 +201,74 @@ extern "C" int32_t pkv_paged_attn_decode_partial(
                                              part_o, part_m, part_l, stream_of(stream)));
 }
 
+namespace {
+
+// Checks shared by the decode-step entry points; fills *plan.
+int32_t check_decode_step(const pkv_cache_desc* cache, const void* k_new, const void* v_new,
+                          const void* q, int32_t q_dtype, int32_t B, int32_t num_q_heads,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, float scale, int32_t partition_blocks,
+                          float* sc, pkv::DecodePlan* plan) {
+  int32_t st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (B < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % cache->num_kv_heads) return PKV_ERR_INVALID_ARG;
+  if (q_dtype != PKV_BF16 || cache->kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (!resolve_scale(scale, cache->head_dim, sc)) return PKV_ERR_INVALID_ARG;
+  if (B > kMaxBatch) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  *plan = pkv::plan_decode(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                           max_blocks_per_seq, partition_blocks, q_dtype, cache->kv_dtype);
+  if (!plan->mfma || plan->head_groups != 1) return PKV_ERR_UNSUPPORTED;
+  if (B == 0) return PKV_OK;
+  if (!q || !block_tables || !seq_lens || !k_new || !v_new) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t pkv_paged_attn_decode_step(const pkv_cache_desc* cache, const void* k_new,
+                                              const void* v_new, const void* q, int32_t q_dtype,
+                                              int32_t B, int32_t num_q_heads,
+                                              const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                              float scale, int32_t partition_blocks, void* out,
+                                              float* out_lse, void* ws, size_t ws_bytes,
+                                              void* stream) {
+  float sc;
+  pkv::DecodePlan plan{};
+  const int32_t st = check_decode_step(cache, k_new, v_new, q, q_dtype, B, num_q_heads,
+                                       block_tables, max_blocks_per_seq, seq_lens, scale,
+                                       partition_blocks, &sc, &plan);
+  if (st != PKV_OK || B == 0) return st;
+  if (!out || !aligned16(out)) return PKV_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < plan.ws_bytes || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return PKV_ERR_WORKSPACE;
+  return from_hip(pkv::launch_decode(view(cache), q, q_dtype, B, num_q_heads, block_tables,
+                                     max_blocks_per_seq, seq_lens, sc, plan, out, out_lse, ws,
+                                     stream_of(stream), k_new, v_new));
+}
+
+extern "C" int32_t pkv_paged_attn_decode_step_partial(
+    const pkv_cache_desc* cache, const void* k_new, const void* v_new, const void* q,
+    int32_t q_dtype, int32_t B, int32_t num_q_heads, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale, int32_t partition_blocks,
+    float* part_o, float* part_m, float* part_l, void* stream) {
+  float sc;
+  pkv::DecodePlan plan{};
+  const int32_t st = check_decode_step(cache, k_new, v_new, q, q_dtype, B, num_q_heads,
+                                       block_tables, max_blocks_per_seq, seq_lens, scale,
+                                       partition_blocks, &sc, &plan);
+  if (st != PKV_OK || B == 0) return st;
+  if (!part_o || !part_m || !part_l || !aligned16(part_o)) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_decode_partial(view(cache), q, q_dtype, B, num_q_heads,
+                                             block_tables, max_blocks_per_seq, seq_lens, sc, plan,
+                                             part_o, part_m, part_l, stream_of(stream), k_new,
+                                             v_new));
+}
+
 extern "C" int32_t pkv_paged_attn_prefill(const pkv_cache_desc* cache, const void* q,
                                           int32_t q_dtype, int32_t T, int32_t num_q_heads,
                                           int32_t q_pos0, const int32_t* block_table,

@@ -55,6 +55,10 @@ struct DecodeParams {
   float* part_o;             // [P][B*hq][D], unnormalised, relative to part_m
   float* part_m;             // [P][B*hq], natural-log units
   float* part_l;             // [P][B*hq]
+  // Folded append (bf16 pools): token seq_lens[b]-1 of sequence b takes
+  // k_new/v_new[b][kv head][:] (bf16); null when the step appends nothing.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
 };
 
 __device__ __forceinline__ int seq_len_clamped(const DecodeParams& p, int b) {
@@ -177,6 +181,43 @@ __device__ __forceinline__ void compute_page(SoftState<D>& st, const BF16Page<D>
     const u32x2 vv = pg.vfrag(nn) & keep;
     st.o[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv), pb_lo,
                                                         st.o[nn], 0, 0, 0);
+  }
+}
+
+// Folded append: the newest token (slot `slot` of this page) is taken from
+// k_new / v_new instead of the pool, and written into the pool by the same
+// lanes.  Lane l holds K of token l%16 (dims 32c + 8*(l/16) .. +8) and V of
+// tokens 4*(l/16) .. +4 (dim 16n + l%16), so the token's K sits in the 4 lanes
+// with l%16 == slot and its V in the 16 lanes with l/16 == slot/4.  Nothing
+// else reads this page in the launch, so the stores race with no load that
+// matters (the page's own load of the slot is replaced here).
+template <int D>
+__device__ __forceinline__ void fold_new_token(BF16Page<D>& pg, const DecodeParams& p, int b,
+                                               int kvh, int blk, int slot, int col, int grp) {
+  const int lane = grp * 16 + col;
+  const int64_t base = (int64_t)blk * p.block_stride_bytes;
+  uint8_t* kp = const_cast<uint8_t*>(p.k) + base + (int64_t)kvh * kBlock * D * 2;
+  uint8_t* vp = const_cast<uint8_t*>(p.v) + base + (int64_t)kvh * D * kBlock * 2;
+  const uint16_t* kn = p.k_new + ((int64_t)b * p.hkv + kvh) * D;
+  const uint16_t* vn = p.v_new + ((int64_t)b * p.hkv + kvh) * D;
+  if (col == slot) {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(kn + 32 * c + 8 * grp);
+      pg.k[c] = x;
+      *reinterpret_cast<u32x4*>(kp + c * 1024 + lane * 16) = x;
+    }
+  }
+  if (grp == (slot >> 2)) {
+    const int wi = (slot & 3) >> 1, sh = 16 * (slot & 1);
+#pragma unroll
+    for (int nn = 0; nn < D / 16; ++nn) {
+      const uint16_t x = vn[16 * nn + col];
+      const int wd = 2 * (nn & 1) + wi;
+      pg.v[nn >> 1][wd] = (pg.v[nn >> 1][wd] & ~(0xffffu << sh)) | ((uint32_t)x << sh);
+      *reinterpret_cast<uint16_t*>(vp + (nn >> 1) * 1024 + lane * 16 + (nn & 1) * 8 +
+                                   (slot & 3) * 2) = x;
+    }
   }
 }
 
@@ -350,6 +391,23 @@ __global__ __launch_bounds__(kThreads, 3) void decode_mfma_kernel(DecodeParams p
   // is peeled), so the count of loads outstanding at each compute is fixed
   // and only the page being computed is waited for.  Table entries are read
   // one step ahead of the loads that need them.
+  // Folded append: this wave's last page is the sequence's last block, which
+  // holds the newest token (the partition holding it has only one workgroup
+  // per kv head: a single 16-head group).
+  bool fold = false;
+  int fold_blk = 0;
+  if constexpr (KVF == PKV_BF16) {
+    const int n_raw = p.seq_lens[b];
+    fold = p.k_new != nullptr && cnt > 0 && n_raw > 0 && n_raw <= p.maxb * kBlock &&
+           pw0 + cnt == nblk;
+    if (fold) fold_blk = trow[nblk - 1];
+  }
+  auto fold_if_last = [&](PageT<D, KVF>& pg, int kk) {
+    if constexpr (KVF == PKV_BF16) {
+      if (fold && kk == cnt - 1)
+        fold_new_token<D>(pg, p, b, kvh, fold_blk, (n - 1) & (kBlock - 1), col, grp);
+    }
+  };
   if (cnt > 0) {
     PageT<D, KVF> pa, pb;
     const int last = cnt - 1;
@@ -368,8 +426,12 @@ __global__ __launch_bounds__(kThreads, 3) void decode_mfma_kernel(DecodeParams p
     if (k + 1 <= last) {
       const bool ok_b = issue_page<D, KVF>(pb, p, tb1, kvh, col, grp);
       if (ok_a) compute_page<D>(st, pa, qf, (pw0 + k) * kBlock + 4 * grp, n, p.scale_log2);
-      if (ok_b) compute_page<D>(st, pb, qf, (pw0 + k + 1) * kBlock + 4 * grp, n, p.scale_log2);
+      if (ok_b) {
+        fold_if_last(pb, k + 1);
+        compute_page<D>(st, pb, qf, (pw0 + k + 1) * kBlock + 4 * grp, n, p.scale_log2);
+      }
     } else if (ok_a) {
+      fold_if_last(pa, k);
       compute_page<D>(st, pa, qf, (pw0 + k) * kBlock + 4 * grp, n, p.scale_log2);
     }
   }
@@ -532,7 +594,8 @@ DecodePlan plan_decode(int B, int hq, int hkv, int head_dim, int maxb, int parti
 hipError_t launch_decode_partial(const CacheView& c, const void* q, int q_dtype, int B, int hq,
                                  const int32_t* tables, int maxb, const int32_t* seq_lens,
                                  float scale, const DecodePlan& plan, float* part_o,
-                                 float* part_m, float* part_l, hipStream_t s) {
+                                 float* part_m, float* part_l, hipStream_t s,
+                                 const void* k_new, const void* v_new) {
   if (B == 0) return hipSuccess;
   const int D = c.head_dim;
   const int esz = c.kv_dtype == PKV_F32 ? 4 : (c.kv_dtype == PKV_BF16 ? 2 : 1);
@@ -559,6 +622,10 @@ hipError_t launch_decode_partial(const CacheView& c, const void* q, int q_dtype,
   p.part_o = part_o;
   p.part_m = part_m;
   p.part_l = part_l;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  if (k_new && !(plan.mfma && plan.head_groups == 1 && c.kv_dtype == PKV_BF16))
+    return hipErrorInvalidValue;            // the fold needs the bf16 MFMA path, one head group
 
   if (plan.mfma) {
     dim3 grid(plan.partitions, c.hkv * plan.head_groups, B), block(kThreads);
@@ -586,7 +653,7 @@ hipError_t launch_decode_partial(const CacheView& c, const void* q, int q_dtype,
 hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, int hq,
                          const int32_t* tables, int maxb, const int32_t* seq_lens, float scale,
                          const DecodePlan& plan, void* out, float* out_lse, void* ws,
-                         hipStream_t s) {
+                         hipStream_t s, const void* k_new, const void* v_new) {
   if (B == 0) return hipSuccess;
   const int D = c.head_dim;
   const size_t rows = (size_t)B * hq * plan.partitions;
@@ -597,7 +664,7 @@ hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, 
   off += (rows * sizeof(float) + 255) & ~size_t(255);
   float* part_l = reinterpret_cast<float*>(w + off);
   hipError_t e = launch_decode_partial(c, q, q_dtype, B, hq, tables, maxb, seq_lens, scale, plan,
-                                       part_o, part_m, part_l, s);
+                                       part_o, part_m, part_l, s, k_new, v_new);
   if (e != hipSuccess) return e;
   return launch_merge(partition_merge_args(plan.partitions, (int64_t)B * hq, D, part_o, part_m,
                                            part_l, out, q_dtype, out_lse),

@@ -121,14 +121,18 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int B, int hq, int hkv, int head_dim, int maxb, int partition_blocks,
                        int q_dtype, int kv_dtype);
+// k_new / v_new (bf16 [B][hkv][D], or null): the folded append of the
+// newest token of every sequence (bf16 MFMA path with one head group only).
 hipError_t launch_decode_partial(const CacheView& c, const void* q, int q_dtype, int B, int hq,
                                  const int32_t* tables, int maxb, const int32_t* seq_lens,
                                  float scale, const DecodePlan& plan, float* part_o,
-                                 float* part_m, float* part_l, hipStream_t s);
+                                 float* part_m, float* part_l, hipStream_t s,
+                                 const void* k_new = nullptr, const void* v_new = nullptr);
 hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, int hq,
                          const int32_t* tables, int maxb, const int32_t* seq_lens, float scale,
                          const DecodePlan& plan, void* out, float* out_lse, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, const void* k_new = nullptr,
+                         const void* v_new = nullptr);
 
 hipError_t launch_prefill(const CacheView& c, const void* q, int T, int hq, int q_pos0,
                           const int32_t* table, int maxb, int kv_begin, int kv_end, int causal,

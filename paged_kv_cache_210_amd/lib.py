@@ -81,6 +81,15 @@ _SIGS = {
     "pkv_paged_attn_decode_partial": (c_int32, [POINTER(CacheDesc), c_void_p, c_int32, c_int32,
                                                 c_int32, c_void_p, c_int32, c_void_p, c_float,
                                                 c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "pkv_paged_attn_decode_step": (c_int32, [POINTER(CacheDesc), c_void_p, c_void_p, c_void_p,
+                                             c_int32, c_int32, c_int32, c_void_p, c_int32,
+                                             c_void_p, c_float, c_int32, c_void_p, c_void_p,
+                                             c_void_p, c_size_t, c_void_p]),
+    "pkv_paged_attn_decode_step_partial": (c_int32, [POINTER(CacheDesc), c_void_p, c_void_p,
+                                                     c_void_p, c_int32, c_int32, c_int32,
+                                                     c_void_p, c_int32, c_void_p, c_float,
+                                                     c_int32, c_void_p, c_void_p, c_void_p,
+                                                     c_void_p]),
     "pkv_paged_attn_prefill": (c_int32, [POINTER(CacheDesc), c_void_p, c_int32, c_int32, c_int32,
                                          c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                          c_float, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -346,6 +355,43 @@ def paged_attn_decode(cache: PagedCache, q, block_tables, seq_lens, scale=0.0,
                                         block_tables.shape[1], _p(seq_lens), float(scale),
                                         int(partition_blocks), _p(out), _p(out_lse), _p(ws),
                                         ws.numel(), _stream(dev)), "paged_attn_decode")
+    return out, out_lse
+
+
+def paged_attn_decode_step(cache: PagedCache, k_new, v_new, q, block_tables, seq_lens, scale=0.0,
+                           partition_blocks=0, out=None, out_lse=None, ws=None, partial=False,
+                           part=None):
+    """pkv_paged_attn_decode_step(_partial): append token seq_lens[b]-1 of every
+    sequence from k_new / v_new ([B, Hkv, d] bf16) and decode, in the decode's
+    own launches.  Returns (out, out_lse), or (part_o, part_m, part_l)."""
+    dev = cache.device
+    B, hq, D = q.shape
+    _need(q, torch.bfloat16, "q", dev)
+    _need(k_new, torch.bfloat16, "k_new", dev, (B, cache.hkv, D))
+    _need(v_new, torch.bfloat16, "v_new", dev, (B, cache.hkv, D))
+    _need(block_tables, torch.int32, "block_tables", dev)
+    _need(seq_lens, torch.int32, "seq_lens", dev, (B,))
+    d = cache.desc()
+    head = (ctypes.byref(d), _p(k_new), _p(v_new), _p(q), PKV_BF16, B, hq, _p(block_tables),
+            block_tables.shape[1], _p(seq_lens), float(scale), int(partition_blocks))
+    if partial:
+        if part is None:
+            P = decode_partitions(cache, q.dtype, B, hq, block_tables.shape[1], partition_blocks)
+            part = (torch.empty(P, B, hq, D, dtype=torch.float32, device=dev),
+                    torch.empty(P, B, hq, dtype=torch.float32, device=dev),
+                    torch.empty(P, B, hq, dtype=torch.float32, device=dev))
+        _check(load().pkv_paged_attn_decode_step_partial(*head, _p(part[0]), _p(part[1]),
+                                                         _p(part[2]), _stream(dev)),
+               "paged_attn_decode_step_partial")
+        return part
+    if out is None:
+        out = torch.empty_like(q)
+    if out_lse is None:
+        out_lse = torch.empty(B, hq, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = decode_workspace(cache, q, block_tables, partition_blocks)
+    _check(load().pkv_paged_attn_decode_step(*head, _p(out), _p(out_lse), _p(ws), ws.numel(),
+                                             _stream(dev)), "paged_attn_decode_step")
     return out, out_lse
 
 
