@@ -37,10 +37,11 @@ __global__ __launch_bounds__(CT) void copy_blocks_kernel(CopyArgs a) {
     dk[o] = k;
     dv[o] = v;
   }
-  if (a.src_ks && blockIdx.y == 0 && (int)threadIdx.x < a.hkv) {
-    const int h = threadIdx.x;
-    a.dst_ks[(int64_t)db * a.hkv + h] = a.src_ks[(int64_t)sb * a.hkv + h];
-    a.dst_vs[(int64_t)db * a.hkv + h] = a.src_vs[(int64_t)sb * a.hkv + h];
+  if (a.src_ks && blockIdx.y == 0) {
+    for (int h = threadIdx.x; h < a.hkv; h += CT) {
+      a.dst_ks[(int64_t)db * a.hkv + h] = a.src_ks[(int64_t)sb * a.hkv + h];
+      a.dst_vs[(int64_t)db * a.hkv + h] = a.src_vs[(int64_t)sb * a.hkv + h];
+    }
   }
 }
 
