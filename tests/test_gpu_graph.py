@@ -1,6 +1,7 @@
 """A decode step (kv_append of one token per sequence + split-KV decode + LSE
-merge) captured in a HIP graph and replayed: every replay, with unrelated
-eager work between replays, must give bit for bit what the eager step gives."""
+merge, or the same with the append folded into the decode launch) captured in
+a HIP graph and replayed: every replay, with unrelated eager work between
+replays, must give bit for bit what the eager step gives."""
 import pytest
 import torch
 
@@ -18,8 +19,12 @@ def lib():
     return L
 
 
-@pytest.mark.parametrize("kv_dtype,pb", [("bf16", 0), ("bf16", 4), ("e4m3", 2)])
-def test_decode_step_graph_replays_match_eager(lib, kv_dtype, pb):
+@pytest.mark.parametrize("kv_dtype,pb,folded", [("bf16", 0, False), ("bf16", 4, False),
+                                                ("e4m3", 2, False), ("bf16", 0, True),
+                                                ("bf16", 4, True)])
+def test_decode_step_graph_replays_match_eager(lib, kv_dtype, pb, folded):
+    """folded: the step is pkv_paged_attn_decode_step_partial (append inside
+    the decode launch) + merge instead of append + decode + merge."""
     cfg = synth.decode_config("graph", (300, 1000, 17, 64), 16, 4, 128, q_dtype="bf16",
                               kv_dtype=kv_dtype, seed_index=31)
     host = synth.decode_inputs(cfg, device="cpu")
@@ -43,8 +48,13 @@ def test_decode_step_graph_replays_match_eager(lib, kv_dtype, pb):
             torch.empty(B, hq, device=DEV)
 
     def step(part, out, lse):
-        lib.kv_append(cache, k1, v1, seq, pos, td)
-        lib.paged_attn_decode_partial(cache, inp["q"], td, lens, partition_blocks=pb, part=part)
+        if folded:
+            lib.paged_attn_decode_step(cache, k1, v1, inp["q"], td, lens, partition_blocks=pb,
+                                       partial=True, part=part)
+        else:
+            lib.kv_append(cache, k1, v1, seq, pos, td)
+            lib.paged_attn_decode_partial(cache, inp["q"], td, lens, partition_blocks=pb,
+                                          part=part)
         lib.attn_lse_merge(*part, out=out, with_state=False, out_lse=lse)
 
     pe, oe, le = buffers()
