@@ -121,6 +121,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 // aligned part rows.
 constexpr int kFewParts = 16;
 
+template <int NS>     // number of parts (a.S), compile-time so every load is in flight at once
 __global__ __launch_bounds__(256) void merge_rows_kernel(MergeArgs a) {
   const int lanes = a.D >> 2;                            // lanes per row
   const int rpw = 64 / lanes;                            // rows per wave (>= 1)
@@ -132,26 +133,31 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(MergeArgs a) {
   const float* mrow = a.m + row * a.ml_row;
   const float* lrow = a.l + row * a.ml_row;
   const float f = kLog2e;               // m in natural units
-  float ms[kFewParts], ls[kFewParts];
+  const float* orow = a.o + row * a.o_row + 4 * li;
+  // every part's m, l and O~ are loaded at once (all parts' rows exist), so
+  // the row costs one memory round trip; parts without keys are selected away
+  // afterwards, never multiplied (their O~ may hold anything)
+  float ms[NS], ls[NS];
+  f32x4 ov[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    ms[s] = mrow[s * a.ml_part];
+    ls[s] = lrow[s * a.ml_part];
+    ov[s] = *reinterpret_cast<const f32x4*>(orow + s * a.o_part);
+  }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kFewParts; ++s) {
-    if (s < a.S) {
-      ms[s] = mrow[s * a.ml_part];
-      ls[s] = lrow[s * a.ml_part];
-      if (ls[s] > 0.f && ms[s] > -INFINITY) M = fmaxf(M, ms[s]);
-    }
-  }
+  for (int s = 0; s < NS; ++s)
+    if (ls[s] > 0.f && ms[s] > -INFINITY) M = fmaxf(M, ms[s]);
   const bool any = M > -INFINITY;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  const float* orow = a.o + row * a.o_row + 4 * li;
 #pragma unroll
-  for (int s = 0; s < kFewParts; ++s) {
-    if (s < a.S && any && ls[s] > 0.f && ms[s] > -INFINITY) {
+  for (int s = 0; s < NS; ++s) {
+    if (any && ls[s] > 0.f && ms[s] > -INFINITY) {
       const float ws = __builtin_amdgcn_exp2f((ms[s] - M) * f);
       L += ws * ls[s];
-      acc += ws * *reinterpret_cast<const f32x4*>(orow + s * a.o_part);
+      acc += ws * ov[s];
     }
   }
   const bool empty = !any || !(L > 0.f);
@@ -185,7 +191,17 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   if (a.S <= kFewParts && vec4 && 64 % (a.D / 4) == 0) {
     const int rpw = 64 / (a.D / 4);
     const int64_t waves = (a.rows + rpw - 1) / rpw;
-    hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    switch (a.S) {
+#define PKV_MERGE_ROWS(n) \
+  case n: hipLaunchKernelGGL(merge_rows_kernel<n>, grid, block, 0, s, a); break;
+      PKV_MERGE_ROWS(1) PKV_MERGE_ROWS(2) PKV_MERGE_ROWS(3) PKV_MERGE_ROWS(4)
+      PKV_MERGE_ROWS(5) PKV_MERGE_ROWS(6) PKV_MERGE_ROWS(7) PKV_MERGE_ROWS(8)
+      PKV_MERGE_ROWS(9) PKV_MERGE_ROWS(10) PKV_MERGE_ROWS(11) PKV_MERGE_ROWS(12)
+      PKV_MERGE_ROWS(13) PKV_MERGE_ROWS(14) PKV_MERGE_ROWS(15) PKV_MERGE_ROWS(16)
+#undef PKV_MERGE_ROWS
+      default: return hipErrorInvalidValue;
+    }
   } else if (vec4) {
     hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)a.rows), dim3(kMergeThreads), 0, s, a);
   } else {
