@@ -19,7 +19,9 @@
 // softmax weights are already laid out as the B operand of the second
 // product.  V is converted to fp16 as it is staged (exact for bf16 values
 // within fp16's range) so the weights enter P V with 11 significant bits
-// instead of bf16's 8.
+// instead of bf16's 8.  Over E4M3 pools ([P2] section 3.2) both products run
+// in fp16: K is staged as its exact codes with each page's K scale applied
+// to the scores, V dequantised while staged, q converted once.
 //
 // Workgroup = 8 waves = the NH query heads of one kv head that share K/V x NR
 // blocks of 32 query rows (NH * NR = 8).  A 64-token K/V tile (4 pages) is
