@@ -127,3 +127,38 @@ def test_decode_step_refuses_what_it_cannot_fold(lib):
     with pytest.raises(lib.PkvError) as e:            # E4M3 pools: append + decode instead
         lib.paged_attn_decode_step(e4, kn, vn, inp["q"].to(DEV), td, lens_d)
     assert e.value.status == lib.PKV_ERR_UNSUPPORTED
+
+
+def test_decode_step_c2_full_size_as_bench_runs_it(lib):
+    """The Llama-3-8B-like layer (32 x 8192, 32 q / 8 kv heads) in the launch
+    configuration bench.py times: pkv_paged_attn_decode_step_partial (library
+    partitioning) + pkv_attn_lse_merge.  Pool and output bitwise against the
+    two-call path; sampled sequences against the oracle."""
+    cfg = synth.CONFIGS["C2"]
+    inp = synth.decode_inputs(cfg, device=DEV)
+    tables, _ = lib.build_tables(cfg.seq_lens, cfg.pool_blocks, inp["free_order"])
+    td = tables.to(DEV)
+    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, 128, "bf16", fill=float("nan"))
+    lens_l = list(cfg.seq_lens)
+    ends = torch.tensor(lens_l, device=DEV).cumsum(0) - 1
+    keep = torch.ones(cfg.num_tokens, dtype=torch.bool, device=DEV)
+    keep[ends] = False
+    seq_idx, pos = inp["seq_idx"].to(DEV), inp["pos"].to(DEV)
+    lib.kv_append(cache, inp["k"][keep].contiguous(), inp["v"][keep].contiguous(),
+                  seq_idx[keep].contiguous(), pos[keep].contiguous(), td)
+    kn, vn = inp["k"][ends].contiguous(), inp["v"][ends].contiguous()
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=DEV)
+    q = inp["q"]
+    ref, rout, rlse, _ = _reference(lib, cache, kn, vn, q, td, lens, lens_l, 0)
+    part = lib.paged_attn_decode_step(cache, kn, vn, q, td, lens, partial=True)
+    out, _, _, lse = lib.attn_lse_merge(*part, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert _same_bits(cache.k, ref.k) and _same_bits(cache.v, ref.v)
+    assert _same_bits(out.view(q.shape), rout)
+    del ref
+    seqs = [0, 17, 31]
+    host = {"k": inp["k"].cpu(), "v": inp["v"].cpu()}
+    oc = oracle_cache(cfg, host, tables.numpy(), seqs=seqs)
+    want = O.decode(oc, bits(q[seqs]), "bf16", tables.numpy()[seqs], [lens_l[b] for b in seqs])
+    compare_rows(out.view(q.shape)[seqs].float().cpu().numpy(), want["o"], "bf16",
+                 "C2 decode step (sampled)")
