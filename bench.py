@@ -79,8 +79,10 @@ def _decode_setup(cfg, partition_blocks):
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
     del inp, keep
     torch.cuda.synchronize()
-    # the folded step needs a bf16 pool and at most 16 query heads per kv head
-    folded = cfg.kv_dtype == "bf16" and cfg.q_dtype == "bf16" and cfg.hq // cfg.hkv <= 16
+    # the folded step needs bf16 q, a bf16 or E4M3 pool and at most 16 query
+    # heads per kv head
+    folded = (cfg.q_dtype == "bf16" and cfg.kv_dtype in ("bf16", "e4m3") and
+              cfg.hq // cfg.hkv <= 16)
     return dict(cache=cache, caches=(cache, twin), td=td, q=q, lens=lens, part=part, out=out,
                 lse=lse, step_in=step_in, tables=tables, partitions=P, folded=folded)
 
@@ -89,10 +91,10 @@ def bench_decode(cfg, steps, warmup, partition_blocks=0):
     """Returns (ms per step, ms per split-KV decode kernel, ms per merge, state).
 
     A step appends the newest token of every sequence and attends with it:
-    for bf16 pools pkv_paged_attn_decode_step_partial (the append folded into
-    the decode launch) + pkv_attn_lse_merge, the launches of
-    pkv_paged_attn_decode_step; for E4M3 pools pkv_kv_append +
-    pkv_paged_attn_decode_partial + pkv_attn_lse_merge.  Events sit between
+    pkv_paged_attn_decode_step_partial (the append folded into the decode
+    launch) + pkv_attn_lse_merge, the launches of pkv_paged_attn_decode_step
+    (shapes it refuses would take pkv_kv_append + pkv_paged_attn_decode_partial
+    + pkv_attn_lse_merge).  Events sit between
     the launches so the dominant kernel is timed on its own.  Steps alternate
     between two pools holding the same KV, so no step reads pages still
     cached from the one before."""

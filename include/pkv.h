@@ -266,8 +266,10 @@ int32_t pkv_paged_attn_decode_partial(const pkv_cache_desc* cache, const void* q
  * count the new token.  The pool ends bit for bit as after pkv_kv_append, and
  * the outputs equal those of the two calls.  Sequences with seq_lens[b] == 0
  * (or beyond the table) append nothing; a block id outside the pool skips the
- * token (as pkv_kv_append does).  bf16 q and bf16 cache only, with at most 16
- * query heads per kv head (otherwise PKV_ERR_UNSUPPORTED: make the two calls).
+ * token (as pkv_kv_append does).  bf16 q; bf16 or E4M3 cache (E4M3: the
+ * token is encoded with its block's scale, which must already be set, as for
+ * pkv_kv_append); at most 16 query heads per kv head (otherwise
+ * PKV_ERR_UNSUPPORTED: make the two calls).
  * Other arguments, workspace and outputs as pkv_paged_attn_decode /
  * pkv_paged_attn_decode_partial. */
 int32_t pkv_paged_attn_decode_step(const pkv_cache_desc* cache, const void* k_new,

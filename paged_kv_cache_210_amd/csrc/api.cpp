@@ -214,7 +214,8 @@ int32_t check_decode_step(const pkv_cache_desc* cache, const void* k_new, const 
   if (B < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_blocks < 0)
     return PKV_ERR_INVALID_ARG;
   if (num_q_heads % cache->num_kv_heads) return PKV_ERR_INVALID_ARG;
-  if (q_dtype != PKV_BF16 || cache->kv_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (q_dtype != PKV_BF16 || (cache->kv_dtype != PKV_BF16 && cache->kv_dtype != PKV_FP8_E4M3))
+    return PKV_ERR_UNSUPPORTED;
   if (!resolve_scale(scale, cache->head_dim, sc)) return PKV_ERR_INVALID_ARG;
   if (B > kMaxBatch) return PKV_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE > INT32_MAX) return PKV_ERR_INVALID_ARG;

@@ -200,23 +200,34 @@ __device__ __forceinline__ void fold_new_token(BF16Page<D>& pg, const DecodePara
   uint8_t* vp = const_cast<uint8_t*>(p.v) + base + (int64_t)kvh * D * kBlock * 2;
   const uint16_t* kn = p.k_new + ((int64_t)b * p.hkv + kvh) * D;
   const uint16_t* vn = p.v_new + ((int64_t)b * p.hkv + kvh) * D;
-  if (col == slot) {
+  // every read of the token before any store: the stores could alias the
+  // inputs as far as the compiler knows, and would otherwise serialise them
+  const bool has_k = col == slot, has_v = grp == (slot >> 2);
+  u32x4 kx[D / 32];
+  uint16_t vx[D / 16];
+  if (has_k) {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) kx[c] = *reinterpret_cast<const u32x4*>(kn + 32 * c + 8 * grp);
+  }
+  if (has_v) {
+#pragma unroll
+    for (int nn = 0; nn < D / 16; ++nn) vx[nn] = vn[16 * nn + col];
+  }
+  if (has_k) {
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(kn + 32 * c + 8 * grp);
-      pg.k[c] = x;
-      *reinterpret_cast<u32x4*>(kp + c * 1024 + lane * 16) = x;
+      pg.k[c] = kx[c];
+      *reinterpret_cast<u32x4*>(kp + c * 1024 + lane * 16) = kx[c];
     }
   }
-  if (grp == (slot >> 2)) {
+  if (has_v) {
     const int wi = (slot & 3) >> 1, sh = 16 * (slot & 1);
 #pragma unroll
     for (int nn = 0; nn < D / 16; ++nn) {
-      const uint16_t x = vn[16 * nn + col];
       const int wd = 2 * (nn & 1) + wi;
-      pg.v[nn >> 1][wd] = (pg.v[nn >> 1][wd] & ~(0xffffu << sh)) | ((uint32_t)x << sh);
+      pg.v[nn >> 1][wd] = (pg.v[nn >> 1][wd] & ~(0xffffu << sh)) | ((uint32_t)vx[nn] << sh);
       *reinterpret_cast<uint16_t*>(vp + (nn >> 1) * 1024 + lane * 16 + (nn & 1) * 8 +
-                                   (slot & 3) * 2) = x;
+                                   (slot & 3) * 2) = vx[nn];
     }
   }
 }
@@ -294,6 +305,60 @@ __device__ __forceinline__ void compute_page(SoftState<D>& st, const FP8Page<D>&
                                                  0);
 #pragma unroll
   for (int nn = 0; nn < D / 16; ++nn) st.o[nn] += t[nn] * vf;
+}
+
+// Folded append into an E4M3 page: the token is encoded exactly as
+// pkv_kv_append encodes it, E4M3(f32(x) * f32(1 / scale)) with the page's
+// scale (set beforehand, as for pkv_kv_append).  Lanes with l%16 == slot
+// hold its K codes (piece i: dims 32c + 8*(l/16) .. +8 for c = 2i, 2i+1);
+// lanes with l/16 == slot/4 hold its V codes (byte slot%4 of word n%4 of
+// piece n/4, dim 16n + l%16).
+template <int D>
+__device__ __forceinline__ void fold_new_token(FP8Page<D>& pg, const DecodeParams& p, int b,
+                                               int kvh, int blk, int slot, int col, int grp) {
+  const int lane = grp * 16 + col;
+  const int64_t base = (int64_t)blk * p.block_stride_bytes;
+  uint8_t* kp = const_cast<uint8_t*>(p.k) + base + (int64_t)kvh * kBlock * D;
+  uint8_t* vp = const_cast<uint8_t*>(p.v) + base + (int64_t)kvh * D * kBlock;
+  const uint16_t* kn = p.k_new + ((int64_t)b * p.hkv + kvh) * D;
+  const uint16_t* vn = p.v_new + ((int64_t)b * p.hkv + kvh) * D;
+  // every read of the token before any store (see the bf16 fold)
+  const bool has_k = col == slot, has_v = grp == (slot >> 2);
+  u32x4 kx[D / 32];                         // bf16 K[32c + 8*grp .. +8], c < D/32
+  uint16_t vx[D / 16];
+  if (has_k) {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) kx[c] = *reinterpret_cast<const u32x4*>(kn + 32 * c + 8 * grp);
+  }
+  if (has_v) {
+#pragma unroll
+    for (int nn = 0; nn < D / 16; ++nn) vx[nn] = vn[16 * nn + col];
+  }
+  if (has_k) {
+    const float inv_k = __frcp_rn(pg.ks);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      u32x4 codes = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t w = kx[2 * i + (e >> 3)][(e & 7) >> 1];
+        const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xffffu);
+        codes[e >> 2] |= e4m3_encode(__fmul_rn(bf16_bits_to_f32(h), inv_k)) << (8 * (e & 3));
+      }
+      pg.k[i] = codes;
+      *reinterpret_cast<u32x4*>(kp + i * 1024 + lane * 16) = codes;
+    }
+  }
+  if (has_v) {
+    const float inv_v = __frcp_rn(pg.vs);
+    const int sh = 8 * (slot & 3);
+#pragma unroll
+    for (int nn = 0; nn < D / 16; ++nn) {
+      const uint32_t c = e4m3_encode(__fmul_rn(bf16_bits_to_f32(vx[nn]), inv_v));
+      pg.v[nn >> 2][nn & 3] = (pg.v[nn >> 2][nn & 3] & ~(0xffu << sh)) | (c << sh);
+      vp[(nn >> 2) * 1024 + lane * 16 + (nn & 3) * 4 + (slot & 3)] = (uint8_t)c;
+    }
+  }
 }
 
 template <int D, int KVF>
@@ -393,20 +458,18 @@ __global__ __launch_bounds__(kThreads, 3) void decode_mfma_kernel(DecodeParams p
   // one step ahead of the loads that need them.
   // Folded append: this wave's last page is the sequence's last block, which
   // holds the newest token (the partition holding it has only one workgroup
-  // per kv head: a single 16-head group).
+  // per kv head: a single 16-head group).  bf16 and E4M3 pages.
   bool fold = false;
   int fold_blk = 0;
-  if constexpr (KVF == PKV_BF16) {
+  {
     const int n_raw = p.seq_lens[b];
     fold = p.k_new != nullptr && cnt > 0 && n_raw > 0 && n_raw <= p.maxb * kBlock &&
            pw0 + cnt == nblk;
     if (fold) fold_blk = trow[nblk - 1];
   }
   auto fold_if_last = [&](PageT<D, KVF>& pg, int kk) {
-    if constexpr (KVF == PKV_BF16) {
-      if (fold && kk == cnt - 1)
-        fold_new_token<D>(pg, p, b, kvh, fold_blk, (n - 1) & (kBlock - 1), col, grp);
-    }
+    if (fold && kk == cnt - 1)
+      fold_new_token<D>(pg, p, b, kvh, fold_blk, (n - 1) & (kBlock - 1), col, grp);
   };
   if (cnt > 0) {
     PageT<D, KVF> pa, pb;
@@ -624,8 +687,8 @@ hipError_t launch_decode_partial(const CacheView& c, const void* q, int q_dtype,
   p.part_l = part_l;
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
-  if (k_new && !(plan.mfma && plan.head_groups == 1 && c.kv_dtype == PKV_BF16))
-    return hipErrorInvalidValue;            // the fold needs the bf16 MFMA path, one head group
+  if (k_new && !(plan.mfma && plan.head_groups == 1))
+    return hipErrorInvalidValue;            // the fold needs the MFMA path with one head group
 
   if (plan.mfma) {
     dim3 grid(plan.partitions, c.hkv * plan.head_groups, B), block(kThreads);

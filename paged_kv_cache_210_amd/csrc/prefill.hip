@@ -539,7 +539,8 @@ __device__ __forceinline__ void attend_step(RowState<D>& st, const f32x16 (&s_cu
       const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + v_lds_off<D>(kst, 32 * dt + qr, hi));
       st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf), pb[kst],
                                                        st.o[dt], 0, 0, 0);
-    }  __builtin_amdgcn_s_setprio(0);
+    }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D, bool NEG_SCALE, bool F8>

@@ -22,15 +22,26 @@ def lib():
     return L
 
 
-def _setup(lib, lens, hq, hkv, seed, d=128, fill=float("nan")):
+def _setup(lib, lens, hq, hkv, seed, d=128, fill=float("nan"), fmt="bf16"):
     """Pool holding all but the newest token of every sequence (other slots
-    hold `fill`: NaN by default, so stray reads show), plus the newest
-    tokens' K/V."""
-    cfg = synth.decode_config("step", tuple(lens), hq, hkv, d, seed_index=90 + seed)
+    hold `fill`: NaN by default, so stray reads show; E4M3 pools: NaN codes,
+    with every group's scale computed from all its tokens first, newest
+    included), plus the newest tokens' K/V."""
+    cfg = synth.decode_config("step", tuple(lens), hq, hkv, d, seed_index=90 + seed,
+                              kv_dtype=fmt, outlier_prob=0.01 if fmt == "e4m3" else 0.0)
     inp = synth.decode_inputs(cfg)
     tables, _ = lib.build_tables(cfg.seq_lens, cfg.pool_blocks, inp["free_order"])
     td = tables.to(DEV)
-    cache = lib.PagedCache.empty(cfg.pool_blocks, hkv, d, "bf16", fill=fill)
+    if fmt == "e4m3":
+        cache = lib.PagedCache.empty(cfg.pool_blocks, hkv, d, "e4m3", fill=0x7F)
+        start = 0
+        for b, n in enumerate(lens):
+            if n > 0:
+                lib.fp8_group_scales(cache, inp["k"][start:start + n].to(DEV),
+                                     inp["v"][start:start + n].to(DEV), 0, td[b])
+            start += n
+    else:
+        cache = lib.PagedCache.empty(cfg.pool_blocks, hkv, d, "bf16", fill=fill)
     n_tok = cfg.num_tokens
     ends = np.cumsum(lens) - 1
     newest = np.zeros(n_tok, dtype=bool)
@@ -47,8 +58,14 @@ def _setup(lib, lens, hq, hkv, seed, d=128, fill=float("nan")):
     return cfg, inp, tables, td, cache, kn.to(DEV), vn.to(DEV)
 
 
+def _clone(lib, cache):
+    return lib.PagedCache(cache.k.clone(), cache.v.clone(), cache.kv_dtype,
+                          None if cache.k_scale is None else cache.k_scale.clone(),
+                          None if cache.v_scale is None else cache.v_scale.clone())
+
+
 def _reference(lib, cache, kn, vn, q, td, lens_d, lens, pb):
-    ref = lib.PagedCache(cache.k.clone(), cache.v.clone(), cache.kv_dtype)
+    ref = _clone(lib, cache)
     live = [b for b, n in enumerate(lens) if n > 0]
     if live:
         idx = torch.tensor(live, device=DEV)
@@ -65,21 +82,24 @@ def _same_bits(a, b):
                        b.contiguous().view(torch.int16 if b.element_size() == 2 else torch.int32))
 
 
-@pytest.mark.parametrize("lens,hq,hkv,pb", [
-    ((1, 16, 17, 33, 100, 257), 8, 2, 0),     # first token, full page, new page, ragged
-    ((1, 16, 17, 33, 100, 257), 8, 2, 1),     # one block per partition
-    ((300, 0, 513, 48), 16, 2, 7),            # an empty sequence; G = 8
-    ((129, 64, 1000), 32, 2, 0),              # G = 16: still one head group
-    ((77, 200), 4, 4, 3),                     # no grouping
+@pytest.mark.parametrize("lens,hq,hkv,pb,fmt", [
+    ((1, 16, 17, 33, 100, 257), 8, 2, 0, "bf16"),   # first token, full page, new page, ragged
+    ((1, 16, 17, 33, 100, 257), 8, 2, 1, "bf16"),   # one block per partition
+    ((300, 0, 513, 48), 16, 2, 7, "bf16"),          # an empty sequence; G = 8
+    ((129, 64, 1000), 32, 2, 0, "bf16"),            # G = 16: still one head group
+    ((77, 200), 4, 4, 3, "bf16"),                   # no grouping
+    ((1, 16, 17, 65, 100, 257), 8, 2, 0, "e4m3"),   # E4M3 pools: the same cases
+    ((300, 0, 513, 48), 16, 2, 7, "e4m3"),
+    ((129, 64, 1000), 32, 2, 1, "e4m3"),
 ])
-def test_decode_step_equals_append_then_decode(lib, lens, hq, hkv, pb):
-    cfg, inp, tables, td, cache, kn, vn = _setup(lib, lens, hq, hkv, seed=len(lens) + pb)
+def test_decode_step_equals_append_then_decode(lib, lens, hq, hkv, pb, fmt):
+    cfg, inp, tables, td, cache, kn, vn = _setup(lib, lens, hq, hkv, seed=len(lens) + pb, fmt=fmt)
     q = inp["q"].to(DEV)
     lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
     ref, rout, rlse, rpart = _reference(lib, cache, kn, vn, q, td, lens_d, lens, pb)
-    fused = lib.PagedCache(cache.k.clone(), cache.v.clone(), cache.kv_dtype)
+    fused = _clone(lib, cache)
     out, lse = lib.paged_attn_decode_step(fused, kn, vn, q, td, lens_d, partition_blocks=pb)
-    fused2 = lib.PagedCache(cache.k.clone(), cache.v.clone(), cache.kv_dtype)
+    fused2 = _clone(lib, cache)
     part = lib.paged_attn_decode_step(fused2, kn, vn, q, td, lens_d, partition_blocks=pb,
                                       partial=True)
     torch.cuda.synchronize()
@@ -90,9 +110,11 @@ def test_decode_step_equals_append_then_decode(lib, lens, hq, hkv, pb):
     for a, b in zip(part, rpart):
         assert torch.equal(a, b)
     # and against the oracle over every sequence's full token list
+    if fmt == "e4m3":
+        assert torch.equal(fused.k_scale, ref.k_scale) and torch.equal(fused.v_scale, ref.v_scale)
     oc = oracle_cache(cfg, inp, tables.numpy())
     want = O.decode(oc, bits(inp["q"]), "bf16", tables.numpy(), cfg.seq_lens)
-    compare_rows(out.float().cpu().numpy(), want["o"], "bf16", f"decode step {lens}")
+    compare_rows(out.float().cpu().numpy(), want["o"], fmt, f"decode step {lens} {fmt}")
 
 
 def test_decode_step_skips_like_append(lib):
@@ -108,7 +130,7 @@ def test_decode_step_skips_like_append(lib):
     lens_bad = torch.tensor([40, 70 + 16 * td.shape[1], 33], dtype=torch.int32, device=DEV)
     lens_list = [40, 70 + 16 * td.shape[1], 33]
     ref, rout, rlse, _ = _reference(lib, cache, kn, vn, q, td2, lens_bad, lens_list, 0)
-    fused = lib.PagedCache(cache.k.clone(), cache.v.clone(), cache.kv_dtype)
+    fused = _clone(lib, cache)
     out, lse = lib.paged_attn_decode_step(fused, kn, vn, q, td2, lens_bad)
     torch.cuda.synchronize()
     assert _same_bits(fused.k, ref.k) and _same_bits(fused.v, ref.v)
@@ -123,9 +145,9 @@ def test_decode_step_refuses_what_it_cannot_fold(lib):
         q = torch.zeros(2, 64, 128, dtype=torch.bfloat16, device=DEV)
         lib.paged_attn_decode_step(cache, kn, vn, q, td, lens_d)
     assert e.value.status == lib.PKV_ERR_UNSUPPORTED
-    e4 = lib.PagedCache.empty(cfg.pool_blocks, 2, 128, "e4m3")
-    with pytest.raises(lib.PkvError) as e:            # E4M3 pools: append + decode instead
-        lib.paged_attn_decode_step(e4, kn, vn, inp["q"].to(DEV), td, lens_d)
+    f32 = lib.PagedCache.empty(cfg.pool_blocks, 2, 128, "f32")
+    with pytest.raises(lib.PkvError) as e:            # f32 pools: append + decode instead
+        lib.paged_attn_decode_step(f32, kn, vn, inp["q"].to(DEV), td, lens_d)
     assert e.value.status == lib.PKV_ERR_UNSUPPORTED
 
 
