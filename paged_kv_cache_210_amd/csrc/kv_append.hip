@@ -282,21 +282,52 @@ __device__ __forceinline__ float src_abs(const void* p, int64_t i) {
   else return fabsf(load_elem<float>(p, i));
 }
 
-// grid (groups, hkv): largest magnitude over a 64-token group for one head,
-// for K and V; scale = f32(amax / 448), 1 if that is 0 or subnormal.
+// Largest magnitude of the 16-byte piece at byte offset o (fmaxf skips NaN,
+// as the element-wise path does).
 template <int SRC>
+__device__ __forceinline__ float piece_absmax(const void* p, int64_t o, float acc) {
+  const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(p) + o);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (SRC == PKV_BF16) {
+      acc = fmaxf(acc, fabsf(__uint_as_float(x[j] << 16)));
+      acc = fmaxf(acc, fabsf(__uint_as_float(x[j] & 0xffff0000u)));
+    } else {
+      acc = fmaxf(acc, fabsf(__uint_as_float(x[j])));
+    }
+  }
+  return acc;
+}
+
+// grid (groups, hkv): largest magnitude over a 64-token group for one head,
+// for K and V; scale = f32(amax / 448), 1 if that is 0 or subnormal.  VEC:
+// both sources 16-byte aligned, read in 16-byte pieces (head_dim is 64 or
+// 128, so a (token, head) row is a whole number of pieces).
+template <int SRC, bool VEC>
 __global__ __launch_bounds__(256) void fp8_scale_kernel(ScaleParams p) {
   __shared__ float red[2][4];
   const int g = blockIdx.x, h = blockIdx.y;
   const int t0 = g * kScaleGroup;
   const int t1 = min(t0 + kScaleGroup, p.num_tokens);
   float ak = 0.f, av = 0.f;
-  const int n = (t1 - t0) * p.D;
-  for (int e = threadIdx.x; e < n; e += 256) {
-    const int t = t0 + e / p.D, d = e % p.D;
-    const int64_t i = ((int64_t)t * p.hkv + h) * p.D + d;
-    ak = fmaxf(ak, src_abs<SRC>(p.k_src, i));
-    av = fmaxf(av, src_abs<SRC>(p.v_src, i));
+  if constexpr (VEC) {
+    constexpr int ES = SRC == PKV_BF16 ? 2 : 4;
+    const int sh = __builtin_ctz((unsigned)(p.D * ES / 16));   // pieces per row = 2^sh
+    const int n = (t1 - t0) << sh;
+    for (int e = threadIdx.x; e < n; e += 256) {
+      const int t = t0 + (e >> sh), c = e & ((1 << sh) - 1);
+      const int64_t o = (((int64_t)t * p.hkv + h) * p.D) * ES + 16 * c;
+      ak = piece_absmax<SRC>(p.k_src, o, ak);
+      av = piece_absmax<SRC>(p.v_src, o, av);
+    }
+  } else {
+    const int n = (t1 - t0) * p.D;
+    for (int e = threadIdx.x; e < n; e += 256) {
+      const int t = t0 + e / p.D, d = e % p.D;
+      const int64_t i = ((int64_t)t * p.hkv + h) * p.D + d;
+      ak = fmaxf(ak, src_abs<SRC>(p.k_src, i));
+      av = fmaxf(av, src_abs<SRC>(p.v_src, i));
+    }
   }
   ak = wave_max(ak);
   av = wave_max(av);
@@ -352,10 +383,15 @@ hipError_t launch_fp8_group_scales(const CacheView& c, float* k_scale, float* v_
   ScaleParams p{k_scale, v_scale, c.hkv, c.head_dim, c.num_blocks, k_src, v_src,
                 num_tokens, pos0, table_row, maxb};
   dim3 grid((num_tokens + kScaleGroup - 1) / kScaleGroup, c.hkv), block(256);
-  if (src_dtype == PKV_BF16)
-    hipLaunchKernelGGL(fp8_scale_kernel<PKV_BF16>, grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL(fp8_scale_kernel<PKV_F32>, grid, block, 0, s, p);
+  const bool vec = ((reinterpret_cast<uintptr_t>(k_src) | reinterpret_cast<uintptr_t>(v_src)) &
+                    15u) == 0 && (c.head_dim == 64 || c.head_dim == 128);
+  if (src_dtype == PKV_BF16) {
+    if (vec) hipLaunchKernelGGL((fp8_scale_kernel<PKV_BF16, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fp8_scale_kernel<PKV_BF16, false>), grid, block, 0, s, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((fp8_scale_kernel<PKV_F32, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fp8_scale_kernel<PKV_F32, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -379,3 +379,37 @@ def test_decode_partial_form_matches_oracle_and_merges_to_decode(lib, pb):
             np.testing.assert_allclose(got_m + np.log(got_l), r["lse"][0], atol=2e-3)
             compare_rows(got_o / got_l[:, None], r["o"][0], "bf16", f"part {p_} seq {b}",
                          out_fmt="f32")
+
+
+def test_fp8_group_scales_aligned_unaligned_and_f32_sources_agree(lib):
+    """The group-scale kernel reads 16-byte pieces when both sources are
+    16-byte aligned and single elements otherwise; bf16 and f32 sources of
+    the same values give the same amax.  All must equal the oracle's scales."""
+    cfg = synth.decode_config("scales", (300,), 8, 2, 128, kv_dtype="e4m3", seed_index=33,
+                              outlier_prob=0.01)
+    inp = synth.decode_inputs(cfg)
+    tables, _ = lib.build_tables(cfg.seq_lens, cfg.pool_blocks, inp["free_order"])
+    td = tables.to(DEV)
+    T = cfg.seq_lens[0]
+    k, v = inp["k"].to(DEV), inp["v"].to(DEV)
+
+    def unaligned(x):
+        buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=DEV)
+        buf[1:] = x.reshape(-1)
+        return buf[1:].view(x.shape)                     # 2 bytes off 16-byte alignment
+
+    got = []
+    for ks, vs in ((k, v), (unaligned(k), unaligned(v)), (k.float(), v.float())):
+        c = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, 128, "e4m3")
+        lib.fp8_group_scales(c, ks, vs, 0, td[0])
+        got.append((c.k_scale.cpu().numpy(), c.v_scale.cpu().numpy()))
+    torch.cuda.synchronize()
+    kn = inp["k"].float().numpy()
+    vn = inp["v"].float().numpy()
+    ref_k = np.ones((cfg.pool_blocks, cfg.hkv), dtype=np.float32)
+    ref_v = np.ones((cfg.pool_blocks, cfg.hkv), dtype=np.float32)
+    O.fp8_group_scales(kn[:T], 0, tables.numpy()[0], ref_k)
+    O.fp8_group_scales(vn[:T], 0, tables.numpy()[0], ref_v)
+    for gk, gv in got:
+        np.testing.assert_array_equal(gk, ref_k)
+        np.testing.assert_array_equal(gv, ref_v)
