@@ -209,16 +209,18 @@ def _prefill_setup(cfg):
             torch.empty(max_parts, C, cfg.hq, dtype=torch.float32, device=dev),
             torch.empty(max_parts, C, cfg.hq, dtype=torch.float32, device=dev))
     out = torch.empty_like(inp["q"])
+    lse1 = torch.empty(C, cfg.hq, dtype=torch.float32, device=dev)
     pos = torch.arange(cfg.prompt_len, dtype=torch.int32, device=dev)
     seq = torch.zeros(C, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
-    return dict(inp=inp, td=td, cache=cache, part=part, out=out, pos=pos, seq=seq)
+    return dict(inp=inp, td=td, cache=cache, part=part, out=out, lse1=lse1, pos=pos, seq=seq)
 
 
 def prefill_pass(cfg, st, ev=None):
     """One chunked pass over the prompt: per chunk append its K/V (for an E4M3
     pool: first the chunk's 64-token group scales), attend to each visible KV
-    shard (partial form), merge the shards by LSE."""
+    shard (partial form), merge the shards by LSE; a chunk that sees a single
+    shard is attended in the final form, with nothing to merge."""
     from paged_kv_cache_210_amd import lib
 
     C, S = cfg.chunk, cfg.shard_len
@@ -234,11 +236,16 @@ def prefill_pass(cfg, st, ev=None):
         nsh = -(-b // S)
         if ev is not None:
             ev.append(("start", c))
-        for j in range(nsh):
-            lib.paged_attn_prefill(cache, q, a, td[0], j * S, min((j + 1) * S, b), True,
-                                   partial=True, part=(po[j, :b - a], pm[j, :b - a], pl[j, :b - a]))
-        lib.attn_lse_merge(po[:nsh, :b - a], pm[:nsh, :b - a], pl[:nsh, :b - a],
-                           out=st["out"][a:b], with_state=False)
+        if nsh == 1:          # one shard holds every visible key: nothing to merge
+            lib.paged_attn_prefill(cache, q, a, td[0], 0, b, True, out=st["out"][a:b],
+                                   out_lse=st["lse1"][:b - a])
+        else:
+            for j in range(nsh):
+                lib.paged_attn_prefill(cache, q, a, td[0], j * S, min((j + 1) * S, b), True,
+                                       partial=True,
+                                       part=(po[j, :b - a], pm[j, :b - a], pl[j, :b - a]))
+            lib.attn_lse_merge(po[:nsh, :b - a], pm[:nsh, :b - a], pl[:nsh, :b - a],
+                               out=st["out"][a:b], with_state=False)
         if ev is not None:
             ev.append(("end", c))
 
