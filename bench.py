@@ -94,10 +94,13 @@ def bench_decode(cfg, steps, warmup, partition_blocks=0):
     pkv_paged_attn_decode_step_partial (the append folded into the decode
     launch) + pkv_attn_lse_merge, the launches of pkv_paged_attn_decode_step
     (shapes it refuses would take pkv_kv_append + pkv_paged_attn_decode_partial
-    + pkv_attn_lse_merge).  Events sit between
-    the launches so the dominant kernel is timed on its own.  Steps alternate
-    between two pools holding the same KV, so no step reads pages still
-    cached from the one before."""
+    + pkv_attn_lse_merge).  In the timed steps two events bracket the decode
+    launch, so the dominant kernel is timed on its own; the merge launch is
+    timed in a pass of its own afterwards, and so is the step with no events
+    at all (reported beside, not as the value: each event recorded between
+    launches costs a few microseconds).  Steps alternate between two pools
+    holding the same KV, so no step reads pages still cached from the one
+    before."""
     import torch
     from paged_kv_cache_210_amd import lib
 
@@ -106,43 +109,54 @@ def bench_decode(cfg, steps, warmup, partition_blocks=0):
     po, pm, pl = st["part"]
     it = [0]
 
-    def step(ev=None):
+    def step(dec_ev=None, merge_ev=None):
         cache = st["caches"][it[0] % 2]
         it[0] += 1
         if st["folded"]:
-            if ev is not None:
-                ev[0].record()
+            if dec_ev is not None:
+                dec_ev[0].record()
             lib.paged_attn_decode_step(cache, s["k"], s["v"], st["q"], st["td"], st["lens"],
                                        partition_blocks=partition_blocks, partial=True,
                                        part=st["part"])
         else:
             lib.kv_append(cache, s["k"], s["v"], s["seq"], s["pos"], st["td"])
-            if ev is not None:
-                ev[0].record()
+            if dec_ev is not None:
+                dec_ev[0].record()
             lib.paged_attn_decode_partial(cache, st["q"], st["td"], st["lens"],
                                           partition_blocks=partition_blocks, part=st["part"])
-        if ev is not None:
-            ev[1].record()
+        if dec_ev is not None:
+            dec_ev[1].record()
+        if merge_ev is not None:
+            merge_ev[0].record()
         lib.attn_lse_merge(po, pm, pl, out=st["out"], with_state=False, out_lse=st["lse"])
-        if ev is not None:
-            ev[2].record()
+        if merge_ev is not None:
+            merge_ev[1].record()
+
+    def timed(k, dec=False, merge=False):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(k)]
+        mevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(k)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(k):
+            step(evs[i] if dec else None, mevs[i] if merge else None)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / k, evs, mevs
 
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(steps):
-        step(evs[i])
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / steps
+    # the timed steps: events only around the decode launch (each event
+    # recorded between launches adds a few microseconds to a step)
+    ms_step, evs, _ = timed(steps, dec=True)
     dec = sorted(e[0].elapsed_time(e[1]) for e in evs)
     st["decode_ms_median"], st["decode_ms_min"] = dec[len(dec) // 2], dec[0]
     ms_dec = sum(dec) / steps
-    ms_merge = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    # after the timed steps: the merge launch on its own, and the step with no
+    # events at all
+    _, _, mevs = timed(steps, merge=True)
+    ms_merge = sum(e[0].elapsed_time(e[1]) for e in mevs) / steps
+    st["ms_per_step_no_events"], _, _ = timed(steps)
     return ms_step, ms_dec, ms_merge, st
 
 
@@ -163,6 +177,7 @@ def decode_record(cfg, steps, warmup, partition_blocks):
         "ms_per_step": ms_step,
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
         "merge_ms": ms_merge,
+        "ms_per_step_no_events": st["ms_per_step_no_events"],
         "partitions": st["partitions"],
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / A.HBM_PEAK_GBS, "traffic": measured_traffic(cfg),
@@ -600,6 +615,8 @@ def main(argv=None):
                    "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
                    "block_size": 16, "kv_dtype": cfg.kv_dtype, "pool_blocks": cfg.pool_blocks,
                    "step": "append 1 token/seq folded into split-KV decode (pkv_paged_attn_decode_step) + LSE merge"},
+        "ms_per_step_no_events": head["ms_per_step_no_events"],
+        "merge_ms": head["merge_ms"],
         "decode_hbm_gbs": head["roofline"]["achieved"],
         "hbm_copy_gbs": copy["gbs"],
         "roofline": head["roofline"],
