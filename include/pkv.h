@@ -25,8 +25,9 @@
  * Conventions
  *  - Ownership: the caller owns every buffer.  Device entry points never
  *    allocate device memory; split-KV decode takes a caller workspace sized by
- *    pkv_decode_workspace_bytes.  Only allocator objects are created by the
- *    library (host memory).
+ *    pkv_decode_workspace_bytes (pkv_paged_attn_decode_noalloc uses a fixed
+ *    static device array of the library instead).  Only allocator objects are
+ *    created by the library (host memory).
  *  - Asynchrony: device entry points enqueue work on `stream` (a hipStream_t
  *    passed as void*, NULL = the null stream) and return without waiting.
  *    pkv_validate_tables is the one exception (it copies to the host).
@@ -60,8 +61,10 @@ enum {
   PKV_ERR_WORKSPACE = -4,    /* workspace missing or too small               */
   PKV_ERR_DEVICE = -5,       /* a HIP runtime call failed                    */
   PKV_ERR_BAD_TABLE = -6,    /* pkv_validate_tables found a bad entry        */
-  PKV_ERR_SHARED = -7        /* a write would land in a block another table
+  PKV_ERR_SHARED = -7,       /* a write would land in a block another table
                                 holds (use pkv_allocator_reserve_cow)        */
+  PKV_ERR_TOO_LARGE = -8     /* the call needs more than the library's static
+                                scratch (PKV_STATIC_SCRATCH_BYTES)           */
 };
 
 /* ---- element types ----------------------------------------------------- */
@@ -73,6 +76,8 @@ enum {
 
 #define PKV_BLOCK_SIZE 16   /* tokens per physical block [P1 2.1, P2 3.1] */
 #define PKV_SCALE_GROUP 64  /* tokens per FP8 scale [P2 3.2]              */
+#define PKV_STATIC_SCRATCH_BYTES (16u << 20)  /* per-device scratch of
+                                                pkv_paged_attn_decode_noalloc */
 
 /* ---- paged KV cache of one attention layer [P1 2.2, P2 3.1] -------------
  * Physical block b, kv head h: the K page starts at
@@ -235,6 +240,26 @@ int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q, int32_
                               int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
                               int32_t partition_blocks, void* out, float* out_lse, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* ---- split-KV decode that allocates nothing ---------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid hipMalloc, harnesses that forbid it):
+ * pkv_paged_attn_decode with the same arguments, results and kernels, minus
+ * the workspace.  The partials live in a static device array of
+ * PKV_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the call uses the copy of the current device (the
+ * stream must belong to it).  A call whose workspace
+ * (pkv_decode_workspace_bytes) exceeds that size returns PKV_ERR_TOO_LARGE
+ * and launches nothing.  No allocation of any kind is made.  The scratch needs
+ * no initialisation (every partial is written before it is read) and keeps
+ * the last call's contents; calls that overlap on one GPU (several streams or
+ * host threads) share it and race, so they must be ordered by the caller. */
+int32_t pkv_paged_attn_decode_noalloc(const pkv_cache_desc* cache, const void* q,
+                                      int32_t q_dtype, int32_t B, int32_t num_q_heads,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, float scale,
+                                      int32_t partition_blocks, void* out, float* out_lse,
+                                      void* stream);
 
 /* ---- split-KV decode, partial form [P4 incremental softmax] -------------------
  * The attention of pkv_paged_attn_decode stopped before the merge, for callers

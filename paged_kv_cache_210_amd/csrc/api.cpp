@@ -68,6 +68,7 @@ extern "C" const char* pkv_status_str(int32_t status) {
     case PKV_ERR_DEVICE: return "HIP runtime error";
     case PKV_ERR_BAD_TABLE: return "block table entry out of range or aliased";
     case PKV_ERR_SHARED: return "write into a block shared with another sequence";
+    case PKV_ERR_TOO_LARGE: return "needs more than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -127,12 +128,15 @@ extern "C" int32_t pkv_decode_workspace_bytes(const pkv_cache_desc* cache, int32
   return PKV_OK;
 }
 
-extern "C" int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q,
-                                         int32_t q_dtype, int32_t B, int32_t num_q_heads,
-                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                         const int32_t* seq_lens, float scale,
-                                         int32_t partition_blocks, void* out, float* out_lse,
-                                         void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Checks shared by pkv_paged_attn_decode and its allocation-free variant;
+// fills *sc and *plan.  PKV_OK with B == 0 means there is nothing to launch.
+int32_t check_decode(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, int32_t B,
+                     int32_t num_q_heads, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
+                     int32_t partition_blocks, const void* out, float* sc,
+                     pkv::DecodePlan* plan) {
   int32_t st = check_cache(cache);
   if (st != PKV_OK) return st;
   if (q_dtype != PKV_F32 && q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
@@ -140,18 +144,56 @@ extern "C" int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void
     return PKV_ERR_INVALID_ARG;
   if (num_q_heads % cache->num_kv_heads) return PKV_ERR_INVALID_ARG;
   if (cache->kv_dtype == PKV_FP8_E4M3 && q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  float sc;
-  if (!resolve_scale(scale, cache->head_dim, &sc)) return PKV_ERR_INVALID_ARG;
+  if (!resolve_scale(scale, cache->head_dim, sc)) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
   if (B > kMaxBatch) return PKV_ERR_UNSUPPORTED;
   if (!q || !block_tables || !seq_lens || !out) return PKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out)) return PKV_ERR_INVALID_ARG;
   if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE > INT32_MAX) return PKV_ERR_INVALID_ARG;
-  pkv::DecodePlan plan = pkv::plan_decode(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                                          max_blocks_per_seq, partition_blocks, q_dtype,
-                                          cache->kv_dtype);
+  *plan = pkv::plan_decode(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                           max_blocks_per_seq, partition_blocks, q_dtype, cache->kv_dtype);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q,
+                                         int32_t q_dtype, int32_t B, int32_t num_q_heads,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* seq_lens, float scale,
+                                         int32_t partition_blocks, void* out, float* out_lse,
+                                         void* ws, size_t ws_bytes, void* stream) {
+  float sc;
+  pkv::DecodePlan plan{};
+  const int32_t st = check_decode(cache, q, q_dtype, B, num_q_heads, block_tables,
+                                  max_blocks_per_seq, seq_lens, scale, partition_blocks, out,
+                                  &sc, &plan);
+  if (st != PKV_OK || B == 0) return st;
   if (!ws || ws_bytes < plan.ws_bytes || (reinterpret_cast<uintptr_t>(ws) & 255u))
     return PKV_ERR_WORKSPACE;
+  return from_hip(pkv::launch_decode(view(cache), q, q_dtype, B, num_q_heads, block_tables,
+                                     max_blocks_per_seq, seq_lens, sc, plan, out, out_lse, ws,
+                                     stream_of(stream)));
+}
+
+// The same decode with its partials in the library's static scratch (the
+// current device's copy): no allocation, no workspace argument.
+extern "C" int32_t pkv_paged_attn_decode_noalloc(const pkv_cache_desc* cache, const void* q,
+                                                 int32_t q_dtype, int32_t B, int32_t num_q_heads,
+                                                 const int32_t* block_tables,
+                                                 int32_t max_blocks_per_seq,
+                                                 const int32_t* seq_lens, float scale,
+                                                 int32_t partition_blocks, void* out,
+                                                 float* out_lse, void* stream) {
+  float sc;
+  pkv::DecodePlan plan{};
+  const int32_t st = check_decode(cache, q, q_dtype, B, num_q_heads, block_tables,
+                                  max_blocks_per_seq, seq_lens, scale, partition_blocks, out,
+                                  &sc, &plan);
+  if (st != PKV_OK || B == 0) return st;
+  if (plan.ws_bytes > pkv::kStaticScratchBytes) return PKV_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (pkv::static_scratch(&ws) != hipSuccess) return PKV_ERR_DEVICE;
   return from_hip(pkv::launch_decode(view(cache), q, q_dtype, B, num_q_heads, block_tables,
                                      max_blocks_per_seq, seq_lens, sc, plan, out, out_lse, ws,
                                      stream_of(stream)));

@@ -10,6 +10,7 @@ namespace pkv {
 
 constexpr int kBlock = PKV_BLOCK_SIZE;   // tokens per physical block
 constexpr int kScaleGroup = PKV_SCALE_GROUP;
+constexpr size_t kStaticScratchBytes = PKV_STATIC_SCRATCH_BYTES;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -133,6 +134,10 @@ hipError_t launch_decode(const CacheView& c, const void* q, int q_dtype, int B, 
                          const DecodePlan& plan, void* out, float* out_lse, void* ws,
                          hipStream_t s, const void* k_new = nullptr,
                          const void* v_new = nullptr);
+
+// Device address of this device's copy of the library's static scratch
+// (kStaticScratchBytes, 256-byte aligned), looked up once per device.
+hipError_t static_scratch(void** out);
 
 hipError_t launch_prefill(const CacheView& c, const void* q, int T, int hq, int q_pos0,
                           const int32_t* table, int maxb, int kv_begin, int kv_end, int causal,

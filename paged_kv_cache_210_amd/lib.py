@@ -23,6 +23,8 @@ PKV_ERR_WORKSPACE = -4
 PKV_ERR_DEVICE = -5
 PKV_ERR_BAD_TABLE = -6
 PKV_ERR_SHARED = -7
+PKV_ERR_TOO_LARGE = -8
+STATIC_SCRATCH_BYTES = 16 << 20     # PKV_STATIC_SCRATCH_BYTES
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 BLOCK_SIZE = 16
@@ -76,6 +78,9 @@ _SIGS = {
     "pkv_paged_attn_decode": (c_int32, [POINTER(CacheDesc), c_void_p, c_int32, c_int32, c_int32,
                                         c_void_p, c_int32, c_void_p, c_float, c_int32, c_void_p,
                                         c_void_p, c_void_p, c_size_t, c_void_p]),
+    "pkv_paged_attn_decode_noalloc": (c_int32, [POINTER(CacheDesc), c_void_p, c_int32, c_int32,
+                                                c_int32, c_void_p, c_int32, c_void_p, c_float,
+                                                c_int32, c_void_p, c_void_p, c_void_p]),
     "pkv_decode_partitions": (c_int32, [POINTER(CacheDesc), c_int32, c_int32, c_int32, c_int32,
                                         c_int32, POINTER(c_int32)]),
     "pkv_paged_attn_decode_partial": (c_int32, [POINTER(CacheDesc), c_void_p, c_int32, c_int32,
@@ -355,6 +360,38 @@ def paged_attn_decode(cache: PagedCache, q, block_tables, seq_lens, scale=0.0,
                                         block_tables.shape[1], _p(seq_lens), float(scale),
                                         int(partition_blocks), _p(out), _p(out_lse), _p(ws),
                                         ws.numel(), _stream(dev)), "paged_attn_decode")
+    return out, out_lse
+
+
+def paged_attn_decode_noalloc(cache: PagedCache, q, block_tables, seq_lens, scale=0.0,
+                              partition_blocks=0, out=None, out_lse=None, with_lse=True):
+    """pkv_paged_attn_decode_noalloc: the decode of paged_attn_decode with its
+    partials in the library's static device scratch (no workspace).  `out`
+    and `out_lse` are made here when not given; a caller that must not
+    allocate passes both (or with_lse=False)."""
+    dev = cache.device
+    B, hq, D = q.shape
+    if D != cache.head_dim:
+        raise ValueError("head_dim mismatch")
+    _need(q, None, "q", dev)
+    qc = _DTYPE_CODE.get(q.dtype)
+    if qc is None:
+        raise TypeError("q must be float32 or bfloat16")
+    _need(block_tables, torch.int32, "block_tables", dev)
+    _need(seq_lens, torch.int32, "seq_lens", dev, (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, q.dtype, "out", dev, q.shape)
+    if out_lse is None and with_lse:
+        out_lse = torch.empty(B, hq, dtype=torch.float32, device=dev)
+    if out_lse is not None:
+        _need(out_lse, torch.float32, "out_lse", dev, (B, hq))
+    d = cache.desc()
+    _check(load().pkv_paged_attn_decode_noalloc(ctypes.byref(d), _p(q), qc, B, hq,
+                                                _p(block_tables), block_tables.shape[1],
+                                                _p(seq_lens), float(scale), int(partition_blocks),
+                                                _p(out), _p(out_lse), _stream(dev)),
+           "paged_attn_decode_noalloc")
     return out, out_lse
 
 
