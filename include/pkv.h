@@ -34,11 +34,15 @@
  *  - Errors: every function returns an int32 status, PKV_OK (0) or a negative
  *    code.  Arguments are checked on the host first; when a check fails
  *    nothing is launched.  pkv_status_str() names a code.
- *  - Table contents are the caller's contract: entries that a sequence length
- *    covers must be distinct valid physical ids.  Kernels never dereference an
- *    id outside [0, num_blocks) (the tokens it would hold are skipped and the
- *    result for that row is then unspecified); pkv_validate_tables reports such
- *    entries and aliasing.
+ *  - Table contents are the caller's contract: the entries a sequence length
+ *    covers must be valid physical ids, distinct within that sequence's table.
+ *    Tables of different sequences may name the same blocks (prefix sharing,
+ *    [P2 3.1]): attention only reads them, and writes into shared blocks are
+ *    the allocator's copy-on-write business (PKV_ERR_SHARED).  Kernels never
+ *    dereference an id outside [0, num_blocks): the tokens such a page would
+ *    hold are skipped (decode) or masked out of the softmax (prefill), and the
+ *    row's result is then that of the remaining keys, which the caller should
+ *    treat as unspecified; pkv_validate_tables reports such entries.
  *  - Reentrancy: functions are reentrant; an allocator object is not
  *    thread-safe.
  */
@@ -63,8 +67,9 @@ enum {
   PKV_ERR_BAD_TABLE = -6,    /* pkv_validate_tables found a bad entry        */
   PKV_ERR_SHARED = -7,       /* a write would land in a block another table
                                 holds (use pkv_allocator_reserve_cow)        */
-  PKV_ERR_TOO_LARGE = -8     /* the call needs more than the library's static
+  PKV_ERR_TOO_LARGE = -8,    /* the call needs more than the library's static
                                 scratch (PKV_STATIC_SCRATCH_BYTES)           */
+  PKV_ERR_OFFLOADED = -9     /* the block is in host memory (page it in first) */
 };
 
 /* ---- element types ----------------------------------------------------- */
@@ -177,6 +182,62 @@ int32_t pkv_allocator_match_prefix(pkv_allocator* a, int32_t seq, const uint64_t
                                    int32_t n, int32_t* matched);
 int32_t pkv_allocator_refcount(const pkv_allocator* a, int32_t block, int32_t* out);
 
+/* ---- KV offload: a host tier of the page table [P3 4.2, 4.3; P1 4] ---------
+ * The allocator's page table records, for every logical block of a sequence,
+ * where it lives (a device block id, or PKV_OFFLOADED in the table and a slot
+ * of a pinned host pool that the caller owns), and the last step that read it.
+ * Offloading and paging in only update that table and return the copy pairs;
+ * the caller moves the data with pkv_copy_blocks (device pool <-> host pool of
+ * the same format), on a stream of its choice, so a page-in (the prefetch)
+ * can run beside the attention of other blocks.  Ordering is the caller's:
+ * a page-in must finish before an attention reads the block, and an offload's
+ * copy must be ordered before anything writes the device block it frees
+ * (that block returns to the free list at once).  Kernels treat PKV_OFFLOADED
+ * entries like any id outside the pool (see the table contract above), so
+ * blocks must be resident when read.  Which blocks to move is the caller's
+ * policy; pkv_allocator_coldest lists the least recently read ones. */
+#define PKV_OFFLOADED (-2)   /* table entry of a block held in a host slot */
+
+/* Give the allocator num_host_slots host slots (ids 0 .. num_host_slots-1 of
+ * the caller's host pool); once per allocator. */
+int32_t pkv_allocator_set_host_slots(pkv_allocator* a, int32_t num_host_slots);
+/* Move the resident blocks among logical blocks [first_block, first_block +
+ * count) of seq (clamped to its table) to host slots: pair i copies device
+ * block dev_ids[i] to host slot host_slots[i] (arrays of at least count
+ * entries), *n_pairs pairs in block order; blocks already offloaded are
+ * skipped.  All-or-nothing: PKV_ERR_SHARED if one of them is held by another
+ * table too, PKV_ERR_NO_BLOCKS if too few host slots are free. */
+int32_t pkv_allocator_offload(pkv_allocator* a, int32_t seq, int32_t first_block, int32_t count,
+                              int32_t* dev_ids, int32_t* host_slots, int32_t* n_pairs);
+/* Bring the offloaded blocks among [first_block, first_block + count) of seq
+ * back: each takes a free device block (from the front of the free list);
+ * pair i copies host slot host_slots[i] to device block dev_ids[i].  The host
+ * slots return to the back of the host free list.  All-or-nothing:
+ * PKV_ERR_NO_BLOCKS if too few device blocks are free. */
+int32_t pkv_allocator_page_in(pkv_allocator* a, int32_t seq, int32_t first_block, int32_t count,
+                              int32_t* host_slots, int32_t* dev_ids, int32_t* n_pairs);
+/* Record that step `step` read blocks [first_block, first_block + count). */
+int32_t pkv_allocator_touch(pkv_allocator* a, int32_t seq, int32_t first_block, int32_t count,
+                            int64_t step);
+/* Page-table entry of logical block `block` of seq: device id (PKV_OFFLOADED
+ * when in host memory), host slot (-1 when resident), last step that read it
+ * (-1 if none). */
+int32_t pkv_allocator_block_state(const pkv_allocator* a, int32_t seq, int32_t block,
+                                  int32_t* device_id, int32_t* host_slot, int64_t* last_access);
+/* The sequence's table as the kernels take it (device ids, PKV_OFFLOADED for
+ * host blocks), up to max_blocks entries (more: PKV_ERR_INVALID_ARG). */
+int32_t pkv_allocator_table(const pkv_allocator* a, int32_t seq, int32_t* table_row,
+                            int32_t max_blocks, int32_t* num_blocks_out);
+int32_t pkv_allocator_host_free_count(const pkv_allocator* a, int32_t* out);
+/* Up to max_n offload candidates, least recently read first (ties: sequence,
+ * then block, ascending): resident full blocks held by one table only. */
+int32_t pkv_allocator_coldest(const pkv_allocator* a, int32_t max_n, int32_t* seqs,
+                              int32_t* blocks, int32_t* n);
+/* Growth that writes into an offloaded last block returns PKV_ERR_OFFLOADED;
+ * fork of a sequence with offloaded blocks returns PKV_ERR_OFFLOADED (host
+ * slots are not shared); publish_prefix skips offloaded blocks; release
+ * returns a sequence's host slots. */
+
 /* ---- kv_append: write new tokens into pool slots [P1 2.2] ----------------
  * For token i < num_tokens: block = block_tables[seq_idx[i]*max_blocks_per_seq
  * + pos[i]/16], slot = pos[i]%16; K page row `slot` <- k_new[i][h][:] and V
@@ -199,14 +260,24 @@ int32_t pkv_kv_append(const pkv_cache_desc* cache, const void* k_new, const void
 
 /* ---- FP8 block-wise scales [P2 3.2] ----------------------------------------
  * For one sequence's tokens [pos0, pos0 + num_tokens) with pos0 % 64 == 0:
- * every 64-token group (aligned to token 0; the last may be shorter) and kv
+ * every 64-token group (aligned to token 0; the last may be partial) and kv
  * head gets scale = f32(amax / 448), amax = largest |x| over the group's
- * tokens and head_dim (1.0 when that quotient is 0 or subnormal), separately
- * for K (from k_src) and V (from v_src).  The scale is stored into
- * k_scale/v_scale[block][head] of every block the group touches, so scales move
- * with blocks.  k_src, v_src: device [num_tokens][num_kv_heads][head_dim] of
- * src_dtype (PKV_F32 | PKV_BF16); table_row: device int32 [max_blocks]
- * covering the tokens. Requires an E4M3 cache. */
+ * given tokens and head_dim (1.0 when that quotient is 0 or subnormal),
+ * separately for K (from k_src) and V (from v_src).  The scale is stored into
+ * k_scale/v_scale[block][head] of every block of the group's 64-token span
+ * that table_row names (entries past max_blocks or outside [0, num_blocks)
+ * are skipped), so scales move with blocks.  k_src, v_src: device
+ * [num_tokens][num_kv_heads][head_dim] of src_dtype (PKV_F32 | PKV_BF16);
+ * table_row: device int32 [max_blocks] covering the tokens. Requires an E4M3
+ * cache.
+ * Policy: a group's scale is fixed by the tokens given when it is computed;
+ * tokens appended to the group later are encoded with it and saturate at
+ * +-448 * scale when larger (pkv_kv_append, the folded decode step).  A
+ * decode stream computes a group's scale from the token that opens it (pos0
+ * = that position, num_tokens = 1), and, when a later token of the group
+ * opens another block, calls again with that same first token, which writes
+ * the same scale into the newly named block.  A prompt computes its scales
+ * from whole groups before appending them. */
 int32_t pkv_fp8_group_scales(const pkv_cache_desc* cache, const void* k_src, const void* v_src,
                              int32_t src_dtype, int32_t num_tokens, int32_t pos0,
                              const int32_t* table_row, int32_t max_blocks, void* stream);
@@ -316,7 +387,15 @@ int32_t pkv_paged_attn_decode_step_partial(const pkv_cache_desc* cache, const vo
  * Row r attends to keys t with kv_begin <= t < kv_end and, when causal, t <=
  * q_pos0 + r, read through block_table (device int32 [max_blocks], covering
  * kv_end).  q: device [T][num_q_heads][head_dim] bf16; a bf16 or E4M3 cache
- * with head_dim 64 or 128 (otherwise PKV_ERR_UNSUPPORTED).  E4M3 pages [P2
+ * with head_dim 64 or 128 (otherwise PKV_ERR_UNSUPPORTED).
+ * bf16 pages: scores use q and K exactly (bf16 products, fp32 sums); V enters
+ * the P V product converted to fp16 with round-toward-zero.  That is exact
+ * for every bf16 value with 2^-14 <= |v| <= 65504 (fp16's normal range);
+ * larger magnitudes saturate to +-65504, and smaller ones are truncated toward
+ * zero to a multiple of 2^-24 (fp16 subnormals; below 2^-24 they become 0),
+ * an absolute change below 6e-8.  So for V outside that range the result is
+ * the attention over the converted V (pkv_paged_attn_decode uses V exactly).
+ * E4M3 pages [P2
  * 3.2]: K is read as its exact codes with each page's K scale applied to the
  * scores in fp32; V is dequantised to fp16 as it is read (f16(code * scale),
  * one rounding); q is converted bf16 -> fp16 and both products run in fp16,
@@ -369,9 +448,8 @@ int32_t pkv_copy_blocks(const pkv_cache_desc* src, const pkv_cache_desc* dst,
  * Copies block_tables / seq_lens (device) to the host after synchronising
  * `stream`, and checks that every entry covered by seq_lens[b] (the first
  * ceil(seq_lens[b]/16)) is in [0, num_blocks) and that no physical block is
- * covered twice (sequences that share blocks through prefix sharing alias
- * by design: check them one at a time).  *first_bad (host) gets -1 when all
- * is well, else the flat
+ * covered twice by one sequence (different sequences may share blocks: prefix
+ * sharing).  *first_bad (host) gets -1 when all is well, else the flat
  * index b*max_blocks_per_seq + j of the first bad entry (status
  * PKV_ERR_BAD_TABLE); a seq_len below 0 or beyond max_blocks_per_seq*16 is
  * reported at index b*max_blocks_per_seq. */

@@ -75,6 +75,13 @@ class SharedBlock(RuntimeError):
     """A growth would write into a partly filled block another table holds."""
 
 
+class Offloaded(RuntimeError):
+    """The block named lives in host memory (it must be paged in first)."""
+
+
+OFFLOADED = -2      # table entry of a block held in a host slot
+
+
 class Allocator:
     """Free list of physical blocks handed out on demand.
 
@@ -90,7 +97,21 @@ class Allocator:
     hashes (computed by the caller) agree.  A growth that writes into a partly
     filled last block held by another table is refused by reserve(); with
     reserve_cow() the sequence first moves onto a fresh block (taken before the
-    growth's own blocks) and the (shared, fresh) pair to copy is returned."""
+    growth's own blocks) and the (shared, fresh) pair to copy is returned.
+
+    KV offload [P3 section 4.2: a page table recording, for every block, the
+    device it is stored on, whether it is swapped out, and when it was last
+    read; pages are brought back ahead of use (prefetch); P1 section 4:
+    blocks not needed for a while move to CPU memory]: with host slots set,
+    offload() moves a sequence's resident blocks to free host slots (their
+    device blocks are freed) and page_in() moves them back to free device
+    blocks; both return the (from, to) copy pairs.  Table entries of
+    offloaded blocks read OFFLOADED.  The readings: only blocks held by a
+    single table move (a shared block is refused); a growth that writes into
+    an offloaded last block, and a fork of a sequence with offloaded blocks,
+    are refused; offloaded blocks are never published; release returns host
+    slots; slots leave from the front of the host free list and return to its
+    back, as device blocks do."""
 
     def __init__(self, num_blocks: int, free_order=None, block_size: int = BLOCK):
         order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
@@ -103,6 +124,10 @@ class Allocator:
         self.refs = [0] * num_blocks
         self.by_hash: dict[int, int] = {}
         self.hash_of: dict[int, int] = {}
+        self.host_free: list[int] = []
+        self.host_slots_set = False
+        self.slot_of: dict[int, list[int]] = {}      # per sequence: host slot per block, -1
+        self.last: dict[int, list[int]] = {}         # per sequence: last step read, -1
 
     def _grow(self, seq, new_len, cow):
         table = list(self.tables.get(seq, []))
@@ -113,6 +138,8 @@ class Allocator:
         refs = list(self.refs)
         pair = None
         writes_tail = new_len > old_len and old_len % self.block_size != 0
+        if writes_tail and table[-1] == OFFLOADED:
+            raise Offloaded(f"sequence {seq} would write into an offloaded block")
         if writes_tail and refs[table[-1]] > 1:
             if not cow:
                 raise SharedBlock(f"sequence {seq} would write into shared block {table[-1]}")
@@ -132,6 +159,9 @@ class Allocator:
                 refs[b] = 1
                 table.append(b)
         self.free, self.refs = free, refs
+        added = len(table) - len(self.tables.get(seq, []))
+        self.slot_of[seq] = self.slot_of.get(seq, []) + [-1] * added
+        self.last[seq] = self.last.get(seq, []) + [-1] * added
         self.tables[seq] = table
         self.lens[seq] = new_len
         return list(table), pair
@@ -146,7 +176,11 @@ class Allocator:
     def fork(self, src: int, dst: int) -> None:
         if src == dst or src not in self.tables or dst in self.tables:
             raise ValueError("fork needs an existing source and a new destination")
+        if OFFLOADED in self.tables[src]:
+            raise Offloaded("host slots are not shared")
         self.tables[dst] = list(self.tables[src])
+        self.slot_of[dst] = [-1] * len(self.tables[src])
+        self.last[dst] = [-1] * len(self.tables[src])
         self.lens[dst] = self.lens[src]
         for b in self.tables[dst]:
             self.refs[b] += 1
@@ -160,6 +194,8 @@ class Allocator:
             raise ValueError("only full blocks can be published")
         for j, h in enumerate(block_hashes):
             b = self.tables[seq][j]
+            if b == OFFLOADED:
+                continue                          # in host memory: not shareable
             if int(h) in self.by_hash or b in self.hash_of:
                 continue                          # the first entry stays
             self.by_hash[int(h)] = b
@@ -176,6 +212,8 @@ class Allocator:
             self.refs[b] += 1
             table.append(b)
         self.tables[seq] = table
+        self.slot_of[seq] = [-1] * len(table)
+        self.last[seq] = [-1] * len(table)
         self.lens[seq] = len(table) * self.block_size
         return len(table)
 
@@ -183,7 +221,12 @@ class Allocator:
         return self.refs[block]
 
     def release(self, seq: int) -> None:
-        for b in self.tables.pop(seq, []):
+        slots = self.slot_of.pop(seq, [])
+        self.last.pop(seq, None)
+        for j, b in enumerate(self.tables.pop(seq, [])):
+            if b == OFFLOADED:
+                self.host_free.append(slots[j])
+                continue
             self.refs[b] -= 1
             if self.refs[b] == 0:
                 h = self.hash_of.pop(b, None)
@@ -197,6 +240,85 @@ class Allocator:
 
     def free_count(self) -> int:
         return len(self.free)
+
+    # ---- host tier ---------------------------------------------------------
+    def set_host_slots(self, n: int) -> None:
+        if self.host_slots_set or n < 0:
+            raise ValueError("host slots are set once")
+        self.host_slots_set = True
+        self.host_free = list(range(n))
+
+    def _range(self, seq, first, count):
+        if seq not in self.tables or first < 0 or count < 0:
+            raise ValueError("unknown sequence or bad range")
+        n = len(self.tables[seq])
+        return range(min(first, n), min(first + count, n))
+
+    def offload(self, seq: int, first: int, count: int):
+        """Move the resident blocks among [first, first + count) to host
+        slots; returns [(device block, host slot)] in block order."""
+        table = self.tables[seq] if seq in self.tables else None
+        js = [j for j in self._range(seq, first, count) if table[j] != OFFLOADED]
+        if any(self.refs[table[j]] > 1 for j in js):
+            raise SharedBlock("a shared block stays on the device")
+        if len(js) > len(self.host_free):
+            raise OutOfBlocks("not enough free host slots")
+        pairs = []
+        for j in js:
+            slot = self.host_free.pop(0)
+            b = table[j]
+            pairs.append((b, slot))
+            self.refs[b] -= 1                    # held by this table only: now free
+            h = self.hash_of.pop(b, None)
+            if h is not None:
+                del self.by_hash[h]
+            self.free.append(b)
+            table[j] = OFFLOADED
+            self.slot_of[seq][j] = slot
+        return pairs
+
+    def page_in(self, seq: int, first: int, count: int):
+        """Bring the offloaded blocks among [first, first + count) back to
+        free device blocks; returns [(host slot, device block)]."""
+        js = [j for j in self._range(seq, first, count) if self.tables[seq][j] == OFFLOADED]
+        if len(js) > len(self.free):
+            raise OutOfBlocks("not enough free device blocks")
+        pairs = []
+        for j in js:
+            b = self.free.pop(0)
+            self.refs[b] = 1
+            slot = self.slot_of[seq][j]
+            pairs.append((slot, b))
+            self.host_free.append(slot)
+            self.tables[seq][j] = b
+            self.slot_of[seq][j] = -1
+        return pairs
+
+    def touch(self, seq: int, first: int, count: int, step: int) -> None:
+        for j in self._range(seq, first, count):
+            self.last[seq][j] = int(step)
+
+    def block_state(self, seq: int, j: int):
+        """(device block or OFFLOADED, host slot or -1, last step read or -1)."""
+        return self.tables[seq][j], self.slot_of[seq][j], self.last[seq][j]
+
+    def table(self, seq: int) -> list[int]:
+        return list(self.tables.get(seq, []))
+
+    def host_free_count(self) -> int:
+        return len(self.host_free)
+
+    def coldest(self, max_n: int):
+        """Offload candidates, least recently read first (ties by sequence,
+        then block): resident full blocks held by one table only."""
+        cand = []
+        for seq, table in self.tables.items():
+            for j in range(min(self.lens[seq] // self.block_size, len(table))):
+                b = table[j]
+                if b != OFFLOADED and self.refs[b] == 1:
+                    cand.append((self.last[seq][j], seq, j))
+        cand.sort()
+        return [(seq, j) for _, seq, j in cand[:max_n]]
 
 
 def build_tables(seq_lens, num_blocks, free_order=None, max_blocks=None):
@@ -282,20 +404,25 @@ def group_scale(amax) -> np.ndarray:
 
 def fp8_group_scales(src, pos0: int, table_row, scale_pool, group: int = SCALE_GROUP):
     """Scales for one sequence's tokens [pos0, pos0 + n), src [n, Hkv, d]
-    (float32 values).  Groups are aligned to token 0; every block of a group
-    receives the group's scale in scale_pool[block, kv_head]."""
+    (float32 values).  Groups are aligned to token 0; a group's scale comes from
+    the given tokens of it, and every block of the group's whole span that the
+    table names (entries at or past its end, and entries -1, are skipped)
+    receives it in scale_pool[block, kv_head].  So a partial group of a
+    decode stream fixes the scale of blocks the table does not hold yet only
+    when they are named (the streaming reading)."""
     src = f32(src)
     n, hkv, _ = src.shape
     if pos0 % group:
         raise ValueError("pos0 must start a scale group")
+    table_row = np.asarray(table_row)
     for g0 in range(0, n, group):
         rows = src[g0:g0 + group]
         amax = np.abs(rows).max(axis=(0, 2))                  # per kv head
         s = group_scale(amax)
         first_tok = pos0 + g0
-        last_tok = pos0 + min(g0 + group, n) - 1
-        for j in range(first_tok // BLOCK, last_tok // BLOCK + 1):
-            scale_pool[int(table_row[j]), :] = s
+        for j in range(first_tok // BLOCK, (first_tok + group - 1) // BLOCK + 1):
+            if j < len(table_row) and 0 <= int(table_row[j]) < scale_pool.shape[0]:
+                scale_pool[int(table_row[j]), :] = s
     return scale_pool
 
 

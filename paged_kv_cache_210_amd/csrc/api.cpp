@@ -69,6 +69,7 @@ extern "C" const char* pkv_status_str(int32_t status) {
     case PKV_ERR_BAD_TABLE: return "block table entry out of range or aliased";
     case PKV_ERR_SHARED: return "write into a block shared with another sequence";
     case PKV_ERR_TOO_LARGE: return "needs more than the library's static scratch";
+    case PKV_ERR_OFFLOADED: return "block is in host memory (page it in first)";
     default: return "unknown status";
   }
 }
@@ -437,7 +438,9 @@ extern "C" int32_t pkv_validate_tables(const int32_t* block_tables, const int32_
       hipMemcpy(lens.data(), seq_lens, lens.size() * sizeof(int32_t), hipMemcpyDeviceToHost) !=
           hipSuccess)
     return PKV_ERR_DEVICE;
-  std::vector<char> used(num_blocks, 0);
+  // seen[id] = the last sequence whose table covered block id: a block may be
+  // named by several sequences (prefix sharing), but only once per table
+  std::vector<int32_t> seen(num_blocks, -1);
   for (int32_t b = 0; b < B; ++b) {
     const int64_t n = lens[b];
     if (n < 0 || n > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE) {
@@ -447,11 +450,11 @@ extern "C" int32_t pkv_validate_tables(const int32_t* block_tables, const int32_
     const int64_t nb = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
     for (int64_t j = 0; j < nb; ++j) {
       const int32_t id = tab[(size_t)b * max_blocks_per_seq + j];
-      if (id < 0 || id >= num_blocks || used[id]) {
+      if (id < 0 || id >= num_blocks || seen[id] == b) {
         *first_bad = (int64_t)b * max_blocks_per_seq + j;
         return PKV_ERR_BAD_TABLE;
       }
-      used[id] = 1;
+      seen[id] = b;
     }
   }
   return PKV_OK;

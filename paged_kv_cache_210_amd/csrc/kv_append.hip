@@ -299,8 +299,9 @@ __device__ __forceinline__ float piece_absmax(const void* p, int64_t o, float ac
   return acc;
 }
 
-// grid (groups, hkv): largest magnitude over a 64-token group for one head,
-// for K and V; scale = f32(amax / 448), 1 if that is 0 or subnormal.  VEC:
+// grid (groups, hkv): largest magnitude over a 64-token group (the given
+// tokens of it) for one head, for K and V; scale = f32(amax / 448), 1 if that
+// is 0 or subnormal.  VEC:
 // both sources 16-byte aligned, read in 16-byte pieces (head_dim is 64 or
 // 128, so a (token, head) row is a whole number of pieces).
 template <int SRC, bool VEC>
@@ -341,7 +342,10 @@ __global__ __launch_bounds__(256) void fp8_scale_kernel(ScaleParams p) {
   float sv = __fdiv_rn(av, 448.0f);
   if (!(sk >= 1.17549435e-38f)) sk = 1.0f;
   if (!(sv >= 1.17549435e-38f)) sv = 1.0f;
-  const int first = p.pos0 + t0, last = p.pos0 + t1 - 1;
+  // every block of the group's 64-token span that the table names takes the
+  // scale (blocks of a partial group not yet in the table get it from a later
+  // call over the group's first tokens)
+  const int first = p.pos0 + t0, last = first + kScaleGroup - 1;
   for (int j = first / kBlock; j <= last / kBlock && j < p.maxb; ++j) {
     const int blk = p.table_row[j];
     if (blk < 0 || blk >= p.num_blocks) continue;

@@ -52,6 +52,10 @@ struct Geo {
   static constexpr int KTILE = TILE;             // K tile: 4 pages as they are in the pool
   static constexpr int BUF = KTILE + TILE;       // one ring slot: K tile + V tile
   static constexpr int LDS = NBUF * BUF;
+  // after the ring, 32 bytes per slot: the tile's four K scales (E4M3 pools)
+  // and one byte per page, 1 when its scores may be used (see page_usable)
+  static constexpr int META = 32;
+  static constexpr int LDS_ALL = LDS + NBUF * META;
   static constexpr int PAGE = kBlock * D * 2;    // bytes of one page
   static constexpr int PAGE8 = kBlock * D;       // bytes of one E4M3 page
   static constexpr int W8 = PAGE8 / 128 / 4;     // 32-bit words of an E4M3 page per staging thread
@@ -123,10 +127,20 @@ __device__ __forceinline__ int tile_entry(const PrefillParams& p, int tile, int 
   return p.table[min(tile * 4 + (tid >> 7), p.maxb - 1)];
 }
 
+// Whether a page's scores may enter the softmax: its block id is in the pool,
+// or none of its tokens lies in [kv_begin, kv_end) (then the position mask
+// hides them anyway).  A page inside the range whose id is outside the pool
+// has its scores masked like positions outside the range, so its keys are
+// skipped as decode skips them.
+__device__ __forceinline__ bool page_usable(const PrefillParams& p, int lblk, bool valid) {
+  return valid || lblk * kBlock >= p.kv_end || (lblk + 1) * kBlock <= p.kv_begin;
+}
+
 // Page loads of a tile.  A page past kv_end or the table, or whose entry is
-// outside the pool, is marked invalid (its V is stored as zeros; its K only
-// ever meets the mask); its loads still run, from block 0, so that no load
-// sits under a branch.  The page, its validity and its address are
+// outside the pool, is marked invalid (its V is stored as zeros; its K is
+// block 0's, and its scores are masked: by position past kv_end, by the
+// tile's page flags otherwise); its loads still run, from block 0, so that
+// no load sits under a branch.  The page, its validity and its address are
 // wave-uniform (scalar).
 //
 // K is moved by global_load_lds_dwordx4: each lane's 16 bytes land at
@@ -195,11 +209,12 @@ __device__ __forceinline__ void put_piece(uint8_t* vs, u32x4 vv, int i, int pg, 
 // is stored as zeros, so masked positions contribute exactly nothing to P V
 // (their K, whatever it holds, only ever meets the mask).
 template <int D>
-__device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs<D>& r,
+__device__ __forceinline__ void store_tile(uint8_t* buf, uint8_t* meta, const TileRegs<D>& r,
                                            const PrefillParams& p, int tile, int tid) {
   uint8_t* vs = buf + Geo<D>::KTILE;
   const int pg = tid >> 7, t128 = tid & 127;
   const int tok_base = tile * BN + pg * kBlock;   // first token of this page
+  if (t128 == 0) meta[16 + pg] = page_usable(p, tile * 4 + pg, r.valid) ? 1 : 0;
   const bool boundary = tile * BN < p.kv_begin || tile * BN + BN > p.kv_end;
   if (r.valid && !boundary) {                      // uniform over the wave
 #pragma unroll
@@ -301,8 +316,9 @@ __device__ __forceinline__ void load_tile(TileRegs8<D>& r, uint8_t*, const Prefi
 // invalid page is stored as zeros (selected, not multiplied, so NaN codes or
 // scales there do not leak).
 template <int D>
-__device__ __forceinline__ void store_tile(uint8_t* buf, float* ks_slot, const TileRegs8<D>& r,
+__device__ __forceinline__ void store_tile(uint8_t* buf, uint8_t* meta, const TileRegs8<D>& r,
                                            const PrefillParams& p, int tile, int tid) {
+  float* ks_slot = reinterpret_cast<float*>(meta);
   constexpr int W8 = Geo<D>::W8;
   uint8_t* vs = buf + Geo<D>::KTILE;
   const int pg = tid >> 7, t128 = tid & 127;
@@ -315,7 +331,10 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, float* ks_slot, const T
                      e4m3x2_f16<false>(r.k[2 * q + 1]), e4m3x2_f16<true>(r.k[2 * q + 1])};
     *reinterpret_cast<u32x4*>(buf + pg * Geo<D>::PAGE + c * 1024 + ((g << 4) + t) * 16) = h;
   }
-  if (t128 == 0) ks_slot[pg] = r.valid ? r.ks : 1.0f;
+  if (t128 == 0) {
+    ks_slot[pg] = r.valid ? r.ks : 1.0f;
+    meta[16 + pg] = page_usable(p, tile * 4 + pg, r.valid) ? 1 : 0;
+  }
   const int tok_base = tile * BN + pg * kBlock;   // first token of this page
   const bool plain = r.valid && !(tile * BN < p.kv_begin || tile * BN + BN > p.kv_end);
 #pragma unroll
@@ -339,18 +358,21 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, float* ks_slot, const T
   }
 }
 
-// Stores a staged tile into ring slot `slot` (and, for E4M3 pools, its K
-// scales into the slot's scale entry after the ring).
-template <int D>
-__device__ __forceinline__ void stage_store(uint8_t* smem, int slot, const TileRegs<D>& r,
+// Stores a staged tile into ring slot `slot`, and its page flags (and, for
+// E4M3 pools, its K scales) into the slot's entry after the ring.
+template <int D, typename Regs>
+__device__ __forceinline__ void stage_store(uint8_t* smem, int slot, const Regs& r,
                                             const PrefillParams& p, int tile, int tid) {
-  store_tile(smem + slot * Geo<D>::BUF, r, p, tile, tid);
+  store_tile(smem + slot * Geo<D>::BUF, smem + Geo<D>::LDS + Geo<D>::META * slot, r, p, tile,
+             tid);
 }
+
+// The four page flags of the tile in ring slot `slot` (byte i = page i),
+// uniform over the workgroup once the barrier publishing the tile is passed.
 template <int D>
-__device__ __forceinline__ void stage_store(uint8_t* smem, int slot, const TileRegs8<D>& r,
-                                            const PrefillParams& p, int tile, int tid) {
-  store_tile(smem + slot * Geo<D>::BUF,
-             reinterpret_cast<float*>(smem + Geo<D>::LDS + 16 * slot), r, p, tile, tid);
+__device__ __forceinline__ uint32_t page_flags(const uint8_t* smem, int slot) {
+  return __builtin_amdgcn_readfirstlane(
+      *reinterpret_cast<const uint32_t*>(smem + Geo<D>::LDS + Geo<D>::META * slot + 16));
 }
 
 // Score product S^T = K Q^T: bf16 operands for bf16 pools, fp16 for E4M3
@@ -411,6 +433,20 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const PrefillParams& p
       s[mt][r] = (ti >= lo && ti < hi_) ? s[mt][r] : hidden;
     }
 }
+
+// Scores of pages flagged unusable (an id outside the pool inside the key
+// range) become the value that scales to -inf.  Page i holds s[i / 2][8 * (i
+// % 2) .. +8] in every lane.
+template <bool NEG_SCALE>
+__device__ __forceinline__ void mask_pages(f32x16 (&s)[2], uint32_t flags) {
+  const float hidden = NEG_SCALE ? INFINITY : -INFINITY;
+#pragma unroll
+  for (int pg = 0; pg < 4; ++pg)
+    if (((flags >> (8 * pg)) & 0xffu) == 0u)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) s[pg >> 1][8 * (pg & 1) + r] = hidden;
+}
+constexpr uint32_t kAllPagesUsable = 0x01010101u;
 
 // Running max for a tile's scores, in log2 units with the scale c folded in
 // (the largest scaled score is c * max(s) for c > 0 and c * min(s) for c < 0).
@@ -608,10 +644,10 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
   if (t_lo <= t_hi) {
     Regs regs;
     load_tile(regs, smem, p, t_lo, tile_entry(p, t_lo, tid), tid, kvh);
-    stage_store(smem, 0, regs, p, t_lo, tid);
+    stage_store<D>(smem, 0, regs, p, t_lo, tid);
     if (t_lo + 1 <= t_hi) {
       load_tile(regs, smem + G::BUF, p, t_lo + 1, tile_entry(p, t_lo + 1, tid), tid, kvh);
-      stage_store(smem, 1, regs, p, t_lo + 1, tid);
+      stage_store<D>(smem, 1, regs, p, t_lo + 1, tid);
     }
     int entry_next = tile_entry(p, t_lo + 2, tid);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct-to-LDS K loads are in
@@ -620,6 +656,10 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
     f32x16 sa[2], sb[2];
     qk_tile<D, F8>(sa, smem, qf, qr, hi);
     if (tile_needs_mask(p, t_lo * BN, w_minpos)) mask_tile<NEG_SCALE>(sa, p, t_lo * BN, my_pos, hi);
+    {
+      const uint32_t fl = page_flags<D>(smem, 0);
+      if (fl != kAllPagesUsable) mask_pages<NEG_SCALE>(sa, fl);
+    }
 
     // Tile j lives in ring slot (j - t_lo) % 3.  Step j starts the loads of
     // tile j+2 (K straight into the slot tile j-1 left, V into registers),
@@ -631,15 +671,19 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
       const int s1 = slot == 2 ? 0 : slot + 1;
       const int s2 = s1 == 2 ? 0 : s1 + 1;
       const bool prefetch = j + 2 <= t_hi;
+      const uint32_t fl_next = page_flags<D>(smem, s1);   // tile j+1, published last step
       Regs nregs;
       if (prefetch) load_tile(nregs, smem + s2 * G::BUF, p, j + 2, entry_next, tid, kvh);
       entry_next = tile_entry(p, j + 3, tid);
       attend_step<D, NEG_SCALE, F8>(st, s_cur, s_next, smem + slot * G::BUF, smem + s1 * G::BUF,
-                                    qf, c, reinterpret_cast<const float*>(smem + G::LDS + 16 * slot),
+                                    qf, c, reinterpret_cast<const float*>(smem + G::LDS + G::META * slot),
                                     qr, hi);
-      if (prefetch) stage_store(smem, s2, nregs, p, j + 2, tid);
-      if (j + 1 <= t_hi && tile_needs_mask(p, (j + 1) * BN, w_minpos))
-        mask_tile<NEG_SCALE>(s_next, p, (j + 1) * BN, my_pos, hi);
+      if (prefetch) stage_store<D>(smem, s2, nregs, p, j + 2, tid);
+      if (j + 1 <= t_hi) {
+        if (tile_needs_mask(p, (j + 1) * BN, w_minpos))
+          mask_tile<NEG_SCALE>(s_next, p, (j + 1) * BN, my_pos, hi);
+        if (fl_next != kAllPagesUsable) mask_pages<NEG_SCALE>(s_next, fl_next);
+      }
       slot = s1;
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct-to-LDS K loads are in
       __syncthreads();
@@ -702,7 +746,7 @@ int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
 // per process and device is enough; repeating it is harmless).
 template <int D, bool NEG, bool F8>
 hipError_t launch_one(const PrefillParams& p, unsigned wgs, hipStream_t s) {
-  constexpr int lds = Geo<D>::LDS + (F8 ? 16 * NBUF : 0);   // E4M3: K scales of each slot
+  constexpr int lds = Geo<D>::LDS_ALL;      // the ring + each slot's flags and K scales
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, NEG, F8>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;

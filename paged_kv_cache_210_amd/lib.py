@@ -24,6 +24,8 @@ PKV_ERR_DEVICE = -5
 PKV_ERR_BAD_TABLE = -6
 PKV_ERR_SHARED = -7
 PKV_ERR_TOO_LARGE = -8
+PKV_ERR_OFFLOADED = -9
+OFFLOADED = -2                      # PKV_OFFLOADED: table entry of a block in a host slot
 STATIC_SCRATCH_BYTES = 16 << 20     # PKV_STATIC_SCRATCH_BYTES
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
@@ -67,6 +69,18 @@ _SIGS = {
     "pkv_allocator_match_prefix": (c_int32, [c_void_p, c_int32, c_void_p, c_int32,
                                              POINTER(c_int32)]),
     "pkv_allocator_refcount": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
+    "pkv_allocator_set_host_slots": (c_int32, [c_void_p, c_int32]),
+    "pkv_allocator_offload": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                        POINTER(c_int32)]),
+    "pkv_allocator_page_in": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                        POINTER(c_int32)]),
+    "pkv_allocator_touch": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int64]),
+    "pkv_allocator_block_state": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_int32),
+                                            POINTER(c_int32), POINTER(c_int64)]),
+    "pkv_allocator_table": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, POINTER(c_int32)]),
+    "pkv_allocator_host_free_count": (c_int32, [c_void_p, POINTER(c_int32)]),
+    "pkv_allocator_coldest": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p,
+                                        POINTER(c_int32)]),
     "pkv_copy_blocks": (c_int32, [POINTER(CacheDesc), POINTER(CacheDesc), c_void_p, c_void_p,
                                   c_int32, c_void_p]),
     "pkv_kv_append": (c_int32, [POINTER(CacheDesc), c_void_p, c_void_p, c_int32, c_int32,
@@ -151,6 +165,20 @@ def _need(t, dtype, name, device=None, shape=None):
         raise ValueError(f"{name} must be on {device}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_q(q, cache, dtype=None):
+    """q [rows, Hq, head_dim] on the cache's device, with Hq a multiple of the
+    cache's kv heads and head_dim the cache's; returns its shape."""
+    _need(q, dtype, "q", cache.device)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [rows, heads, head_dim], got shape {tuple(q.shape)}")
+    rows, hq, D = q.shape
+    if D != cache.head_dim:
+        raise ValueError(f"q head_dim {D} != cache head_dim {cache.head_dim}")
+    if hq % cache.hkv:
+        raise ValueError(f"q heads {hq} not a multiple of the cache's {cache.hkv} kv heads")
+    return rows, hq, D
 
 
 # ---------------------------------------------------------------- cache
@@ -250,6 +278,57 @@ class Allocator:
     def release(self, seq: int):
         _check(load().pkv_allocator_release(self._h, seq), "allocator_release")
 
+    # host tier (KV offload): the C page table; data moves with copy_blocks
+    def set_host_slots(self, n: int):
+        _check(load().pkv_allocator_set_host_slots(self._h, n), "allocator_set_host_slots")
+
+    def _moves(self, fn, seq, first, count, what):
+        k = max(0, int(count))
+        a, b = (c_int32 * max(1, k))(), (c_int32 * max(1, k))()
+        n = c_int32()
+        _check(fn(self._h, seq, int(first), k, a, b, ctypes.byref(n)), what)
+        return list(zip(a[:n.value], b[:n.value]))
+
+    def offload(self, seq: int, first: int, count: int):
+        """[(device block, host slot)] to copy device -> host."""
+        return self._moves(load().pkv_allocator_offload, seq, first, count, "allocator_offload")
+
+    def page_in(self, seq: int, first: int, count: int):
+        """[(host slot, device block)] to copy host -> device."""
+        return self._moves(load().pkv_allocator_page_in, seq, first, count, "allocator_page_in")
+
+    def touch(self, seq: int, first: int, count: int, step: int):
+        _check(load().pkv_allocator_touch(self._h, seq, int(first), int(count), int(step)),
+               "allocator_touch")
+
+    def block_state(self, seq: int, block: int):
+        """(device id or OFFLOADED, host slot or -1, last step read or -1)."""
+        d, h, t = c_int32(), c_int32(), c_int64()
+        _check(load().pkv_allocator_block_state(self._h, seq, block, ctypes.byref(d),
+                                                ctypes.byref(h), ctypes.byref(t)),
+               "allocator_block_state")
+        return d.value, h.value, t.value
+
+    def table(self, seq: int, max_blocks: int = 1 << 20):
+        row = (c_int32 * max_blocks)()
+        n = c_int32()
+        _check(load().pkv_allocator_table(self._h, seq, row, max_blocks, ctypes.byref(n)),
+               "allocator_table")
+        return list(row[:n.value])
+
+    def host_free_count(self) -> int:
+        out = c_int32()
+        _check(load().pkv_allocator_host_free_count(self._h, ctypes.byref(out)),
+               "host_free_count")
+        return out.value
+
+    def coldest(self, max_n: int):
+        a, b = (c_int32 * max(1, max_n))(), (c_int32 * max(1, max_n))()
+        n = c_int32()
+        _check(load().pkv_allocator_coldest(self._h, max_n, a, b, ctypes.byref(n)),
+               "allocator_coldest")
+        return list(zip(a[:n.value], b[:n.value]))
+
     def waste_slots(self, seq: int) -> int:
         out = c_int64()
         _check(load().pkv_allocator_waste_slots(self._h, seq, ctypes.byref(out)), "waste_slots")
@@ -339,10 +418,7 @@ def decode_workspace(cache, q, block_tables, partition_blocks=0):
 def paged_attn_decode(cache: PagedCache, q, block_tables, seq_lens, scale=0.0,
                       partition_blocks=0, out=None, out_lse=None, ws=None, with_lse=True):
     dev = cache.device
-    B, hq, D = q.shape
-    if D != cache.head_dim:
-        raise ValueError("head_dim mismatch")
-    _need(q, None, "q", dev)
+    B, hq, D = _need_q(q, cache)
     qc = _DTYPE_CODE.get(q.dtype)
     if qc is None:
         raise TypeError("q must be float32 or bfloat16")
@@ -353,13 +429,17 @@ def paged_attn_decode(cache: PagedCache, q, block_tables, seq_lens, scale=0.0,
     _need(out, q.dtype, "out", dev, q.shape)
     if out_lse is None and with_lse:
         out_lse = torch.empty(B, hq, dtype=torch.float32, device=dev)
+    if out_lse is not None:
+        _need(out_lse, torch.float32, "out_lse", dev, (B, hq))
     if ws is None:
         ws = decode_workspace(cache, q, block_tables, partition_blocks)
+    _need(ws, None, "ws", dev)
     d = cache.desc()
     _check(load().pkv_paged_attn_decode(ctypes.byref(d), _p(q), qc, B, hq, _p(block_tables),
                                         block_tables.shape[1], _p(seq_lens), float(scale),
                                         int(partition_blocks), _p(out), _p(out_lse), _p(ws),
-                                        ws.numel(), _stream(dev)), "paged_attn_decode")
+                                        ws.numel() * ws.element_size(), _stream(dev)),
+           "paged_attn_decode")
     return out, out_lse
 
 
@@ -370,10 +450,7 @@ def paged_attn_decode_noalloc(cache: PagedCache, q, block_tables, seq_lens, scal
     and `out_lse` are made here when not given; a caller that must not
     allocate passes both (or with_lse=False)."""
     dev = cache.device
-    B, hq, D = q.shape
-    if D != cache.head_dim:
-        raise ValueError("head_dim mismatch")
-    _need(q, None, "q", dev)
+    B, hq, D = _need_q(q, cache)
     qc = _DTYPE_CODE.get(q.dtype)
     if qc is None:
         raise TypeError("q must be float32 or bfloat16")
@@ -402,8 +479,7 @@ def paged_attn_decode_step(cache: PagedCache, k_new, v_new, q, block_tables, seq
     sequence from k_new / v_new ([B, Hkv, d] bf16) and decode, in the decode's
     own launches.  Returns (out, out_lse), or (part_o, part_m, part_l)."""
     dev = cache.device
-    B, hq, D = q.shape
-    _need(q, torch.bfloat16, "q", dev)
+    B, hq, D = _need_q(q, cache, torch.bfloat16)
     _need(k_new, torch.bfloat16, "k_new", dev, (B, cache.hkv, D))
     _need(v_new, torch.bfloat16, "v_new", dev, (B, cache.hkv, D))
     _need(block_tables, torch.int32, "block_tables", dev)
@@ -412,23 +488,30 @@ def paged_attn_decode_step(cache: PagedCache, k_new, v_new, q, block_tables, seq
     head = (ctypes.byref(d), _p(k_new), _p(v_new), _p(q), PKV_BF16, B, hq, _p(block_tables),
             block_tables.shape[1], _p(seq_lens), float(scale), int(partition_blocks))
     if partial:
+        P = decode_partitions(cache, q.dtype, B, hq, block_tables.shape[1], partition_blocks)
         if part is None:
-            P = decode_partitions(cache, q.dtype, B, hq, block_tables.shape[1], partition_blocks)
             part = (torch.empty(P, B, hq, D, dtype=torch.float32, device=dev),
                     torch.empty(P, B, hq, dtype=torch.float32, device=dev),
                     torch.empty(P, B, hq, dtype=torch.float32, device=dev))
+        _need(part[0], torch.float32, "part_o", dev, (P, B, hq, D))
+        _need(part[1], torch.float32, "part_m", dev, (P, B, hq))
+        _need(part[2], torch.float32, "part_l", dev, (P, B, hq))
         _check(load().pkv_paged_attn_decode_step_partial(*head, _p(part[0]), _p(part[1]),
                                                          _p(part[2]), _stream(dev)),
                "paged_attn_decode_step_partial")
         return part
     if out is None:
         out = torch.empty_like(q)
+    _need(out, torch.bfloat16, "out", dev, (B, hq, D))
     if out_lse is None:
         out_lse = torch.empty(B, hq, dtype=torch.float32, device=dev)
+    _need(out_lse, torch.float32, "out_lse", dev, (B, hq))
     if ws is None:
         ws = decode_workspace(cache, q, block_tables, partition_blocks)
-    _check(load().pkv_paged_attn_decode_step(*head, _p(out), _p(out_lse), _p(ws), ws.numel(),
-                                             _stream(dev)), "paged_attn_decode_step")
+    _need(ws, None, "ws", dev)
+    _check(load().pkv_paged_attn_decode_step(*head, _p(out), _p(out_lse), _p(ws),
+                                             ws.numel() * ws.element_size(), _stream(dev)),
+           "paged_attn_decode_step")
     return out, out_lse
 
 
@@ -445,8 +528,7 @@ def paged_attn_decode_partial(cache: PagedCache, q, block_tables, seq_lens, scal
                               partition_blocks=0, part=None):
     """Partial form: returns (part_o [P,B,Hq,d], part_m [P,B,Hq], part_l [P,B,Hq])."""
     dev = cache.device
-    B, hq, D = q.shape
-    _need(q, None, "q", dev)
+    B, hq, D = _need_q(q, cache)
     qc = _DTYPE_CODE.get(q.dtype)
     if qc is None:
         raise TypeError("q must be float32 or bfloat16")
@@ -473,21 +555,27 @@ def paged_attn_decode_partial(cache: PagedCache, q, block_tables, seq_lens, scal
 def paged_attn_prefill(cache: PagedCache, q, q_pos0, block_table, kv_begin, kv_end, causal=True,
                        scale=0.0, partial=False, out=None, out_lse=None, part=None):
     dev = cache.device
-    T, hq, D = q.shape
-    _need(q, torch.bfloat16, "q", dev)
+    T, hq, D = _need_q(q, cache, torch.bfloat16)
     _need(block_table, torch.int32, "block_table", dev)
+    if block_table.dim() != 1:
+        raise ValueError("block_table must be one sequence's table (1-D)")
     if partial:
         if part is None:
             part = (torch.empty(T, hq, D, dtype=torch.float32, device=dev),
                     torch.empty(T, hq, dtype=torch.float32, device=dev),
                     torch.empty(T, hq, dtype=torch.float32, device=dev))
         po, pm, pl = part
+        _need(po, torch.float32, "part_o", dev, (T, hq, D))
+        _need(pm, torch.float32, "part_m", dev, (T, hq))
+        _need(pl, torch.float32, "part_l", dev, (T, hq))
         args = (None, None, _p(po), _p(pm), _p(pl))
     else:
         if out is None:
             out = torch.empty_like(q)
+        _need(out, torch.bfloat16, "out", dev, (T, hq, D))
         if out_lse is None:
             out_lse = torch.empty(T, hq, dtype=torch.float32, device=dev)
+        _need(out_lse, torch.float32, "out_lse", dev, (T, hq))
         args = (_p(out), _p(out_lse), None, None, None)
     d = cache.desc()
     _check(load().pkv_paged_attn_prefill(ctypes.byref(d), _p(q), PKV_BF16, T, hq, int(q_pos0),
@@ -502,21 +590,28 @@ def attn_lse_merge(part_o, part_m, part_l, out_dtype=torch.bfloat16, out=None, w
     """part_o [S, rows..., d] fp32, part_m/part_l [S, rows...]; returns
     (O [rows..., d], M, L, lse)."""
     dev = part_o.device
+    _need(part_o, torch.float32, "part_o", dev)
+    if part_o.dim() < 3:
+        raise ValueError("part_o must be [S, rows..., head_dim]")
     S = part_o.shape[0]
     D = part_o.shape[-1]
     rows_shape = tuple(part_o.shape[1:-1])
     rows = math.prod(rows_shape)
-    _need(part_o, torch.float32, "part_o", dev)
     _need(part_m, torch.float32, "part_m", dev, (S,) + rows_shape)
     _need(part_l, torch.float32, "part_l", dev, (S,) + rows_shape)
     if out is None:
         out = torch.empty(rows_shape + (D,), dtype=out_dtype, device=dev)
+    if out.dtype not in _DTYPE_CODE:
+        raise TypeError("out must be float32 or bfloat16")
+    _need(out, None, "out", dev, rows_shape + (D,))
     m = l = None
     lse = out_lse
     if with_state:
         m = torch.empty(rows_shape, dtype=torch.float32, device=dev)
         l = torch.empty_like(m)
         lse = torch.empty_like(m) if lse is None else lse
+    if lse is not None:
+        _need(lse, torch.float32, "out_lse", dev, rows_shape)
     _check(load().pkv_attn_lse_merge(S, rows, D, _p(part_o), _p(part_m), _p(part_l), _p(out),
                                      _DTYPE_CODE[out.dtype], _p(m), _p(l), _p(lse), _stream(dev)),
            "attn_lse_merge")

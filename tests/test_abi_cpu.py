@@ -232,3 +232,77 @@ def test_copy_blocks_argument_checks(lib):
     assert L.pkv_copy_blocks(ctypes.byref(bf), ctypes.byref(bf), None, ids, 3, None) == \
         lib.PKV_ERR_INVALID_ARG
     assert lib.status_str(lib.PKV_ERR_SHARED).startswith("write into a block shared")
+
+
+def test_offload_page_table_matches_oracle_step_for_step(lib):
+    """The host tier of the C allocator (offload, page-in, touch, coldest,
+    and growth / fork / publish / release around offloaded blocks) against the
+    oracle's page-table model: same copy pairs, tables, block states, free
+    device blocks and host slots, candidates, and refusals."""
+    nb, nh = 36, 20
+    order = synth.free_order(nb, 79).numpy()
+    a = lib.Allocator(nb, order)
+    o = O.Allocator(nb, order)
+    a.set_host_slots(nh)
+    o.set_host_slots(nh)
+    codes = {O.OutOfBlocks: lib.PKV_ERR_NO_BLOCKS, O.SharedBlock: lib.PKV_ERR_SHARED,
+             O.Offloaded: lib.PKV_ERR_OFFLOADED, ValueError: lib.PKV_ERR_INVALID_ARG}
+
+    def same(fo, fa):
+        try:
+            want = fo()
+        except tuple(codes) as ex:
+            with pytest.raises(lib.PkvError) as e:
+                fa()
+            assert e.value.status == codes[type(ex)], ex
+            return None
+        got = fa()
+        assert got == want
+        return got
+
+    r = np.random.default_rng(3)
+    counts = {"offload": 0, "page_in": 0}
+    for step in range(1500):
+        op = r.random()
+        s = int(r.integers(0, 6))
+        if op < 0.3:
+            n = o.lens.get(s, 0) + int(r.integers(0, 30))
+            same(lambda: o.reserve_cow(s, n), lambda: a.reserve_cow(s, n, max_blocks=nb))
+        elif op < 0.5:
+            f, c = int(r.integers(0, 5)), int(r.integers(0, 6))
+            if s in o.tables:
+                counts["offload"] += len(same(lambda: o.offload(s, f, c),
+                                              lambda: a.offload(s, f, c)) or [])
+        elif op < 0.68:
+            f, c = int(r.integers(0, 5)), int(r.integers(0, 6))
+            if s in o.tables:
+                counts["page_in"] += len(same(lambda: o.page_in(s, f, c),
+                                              lambda: a.page_in(s, f, c)) or [])
+        elif op < 0.75:
+            if s in o.tables:
+                f, c, t = int(r.integers(0, 5)), int(r.integers(0, 6)), int(r.integers(0, 50))
+                o.touch(s, f, c, t)
+                a.touch(s, f, c, t)
+        elif op < 0.82:
+            d = int(r.integers(0, 6))
+            same(lambda: o.fork(s, d), lambda: a.fork(s, d))
+        elif op < 0.9:
+            if s in o.tables:
+                hs = [int(x) for x in r.integers(0, 5, size=o.lens[s] // 16)]
+                o.publish_prefix(s, hs)
+                a.publish_prefix(s, hs)
+                d = int(r.integers(0, 6))
+                same(lambda: o.match_prefix(d, hs[:2]), lambda: a.match_prefix(d, hs[:2]))
+        else:
+            a.release(s)
+            o.release(s)
+        assert a.free_count() == o.free_count() and a.host_free_count() == o.host_free_count()
+        for q in range(6):
+            assert a.table(q) == o.table(q), (step, q)
+            for j in range(len(o.table(q))):
+                assert a.block_state(q, j) == o.block_state(q, j), (step, q, j)
+        for b in range(nb):
+            assert a.refcount(b) == o.refcount(b), (step, b)
+        assert a.coldest(nb) == o.coldest(nb), step
+    assert counts["offload"] > 50 and counts["page_in"] > 20
+    a.close()

@@ -324,9 +324,27 @@ def test_validate_tables_flags_bad_entries(lib):
     assert lib.validate_tables(t, lens, 5) == -1
     assert lib.validate_tables(t, lens, 4) == 5                    # id 4 out of range
     t2 = torch.tensor([[0, 1, -1], [2, 1, 4]], dtype=torch.int32, device=DEV)
-    assert lib.validate_tables(t2, lens, 5) == 4                   # block 1 aliased
+    assert lib.validate_tables(t2, lens, 5) == -1                  # shared across sequences: ok
+    t3 = torch.tensor([[0, 1, -1], [2, 4, 2]], dtype=torch.int32, device=DEV)
+    assert lib.validate_tables(t3, lens, 5) == 5                   # block 2 twice in one table
     lens2 = torch.tensor([40, 40], dtype=torch.int32, device=DEV)
     assert lib.validate_tables(t, lens2, 5) == 2                   # -1 covered by a length
+    # tables made by the allocator's fork and prefix match (blocks shared by
+    # design) are valid
+    alloc = lib.Allocator(16)
+    rows = [alloc.reserve(0, 40)]
+    alloc.fork(0, 1)
+    rows.append(alloc.reserve_cow(1, 45)[0])
+    alloc.publish_prefix(0, [11, 12])
+    alloc.match_prefix(2, [11, 12, 13])
+    rows.append(alloc.reserve(2, 50))
+    tf = torch.full((3, 4), -1, dtype=torch.int32)
+    for b, r in enumerate(rows):
+        tf[b, :len(r)] = torch.tensor(r, dtype=torch.int32)
+    lf = torch.tensor([40, 45, 50], dtype=torch.int32, device=DEV)
+    assert alloc.refcount(rows[0][0]) == 3
+    assert lib.validate_tables(tf.to(DEV), lf, 16) == -1
+    alloc.close()
 
 
 def test_decode_workspace_reused_across_calls(lib):

@@ -184,3 +184,114 @@ def test_decode_step_c2_full_size_as_bench_runs_it(lib):
     want = O.decode(oc, bits(q[seqs]), "bf16", tables.numpy()[seqs], [lens_l[b] for b in seqs])
     compare_rows(out.view(q.shape)[seqs].float().cpu().numpy(), want["o"], "bf16",
                  "C2 decode step (sampled)")
+
+
+@pytest.mark.parametrize("folded", [False, True])
+def test_fp8_streaming_group_scales(lib, folded):
+    """An E4M3 pool fed as a decode stream, bit-exact against the oracle.
+
+    Two prompts (192 tokens: whole groups; 100 tokens: group 1 left partial)
+    get their scales from whole prompt calls, then 80 decode steps append one
+    token per sequence, allocating blocks on demand.  A token that opens a
+    64-token group fixes the group's scale alone (pos0 = its position, one
+    token); when a later token of a group opens another block, the call that
+    fixed the group is repeated (same tokens), naming the new block.  Decode
+    tokens that do not open a group are twice as large, so many exceed their
+    group's max and saturate.  Each step appends through pkv_kv_append +
+    pkv_paged_attn_decode, or through the folded pkv_paged_attn_decode_step;
+    the pool (codes and scales) must equal the oracle's bit for bit after
+    every step, and the outputs the oracle's within the FP8 bound."""
+    from tests._util import frag_pages_logical
+    hq, hkv, d = 16, 2, 128
+    prompt, steps = (192, 100), 80
+    total = tuple(n + steps for n in prompt)
+    cfg = synth.decode_config("stream", total, hq, hkv, d, q_dtype="bf16", kv_dtype="e4m3",
+                              seed_index=95)
+    inp = synth.decode_inputs(cfg)
+    B = len(prompt)
+    starts = np.concatenate([[0], np.cumsum(total)[:-1]])
+    k = inp["k"].float().clone()
+    v = inp["v"].float().clone()
+    for b in range(B):                       # decode tokens off a group start: x2
+        for p in range(prompt[b], total[b]):
+            if p % 64:
+                k[starts[b] + p] *= 2
+                v[starts[b] + p] *= 2
+    k, v = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    kf, vf = k.float().numpy(), v.float().numpy()
+
+    maxb = max(-(-n // 16) for n in total)
+    alloc = lib.Allocator(cfg.pool_blocks, inp["free_order"])
+    tab = np.full((B, maxb), -1, dtype=np.int32)
+
+    def grow(b, n):
+        row = alloc.reserve(b, n, maxb)
+        tab[b, :len(row)] = row
+
+    cache = lib.PagedCache.empty(cfg.pool_blocks, hkv, d, "e4m3", fill=0)
+    oc = O.new_cache(cfg.pool_blocks, hkv, d, "e4m3")
+    fixing = {}                               # (b, group) -> (first token, count)
+
+    def scales(b, pos0, t0, cnt):
+        """Both sides: the group scale call over tokens [t0, t0 + cnt) of
+        sequence b (absolute position pos0 of the first)."""
+        td_b = torch.from_numpy(tab[b]).to(DEV)
+        a = starts[b] + t0
+        lib.fp8_group_scales(cache, k[a:a + cnt].to(DEV), v[a:a + cnt].to(DEV), pos0, td_b)
+        O.fp8_group_scales(kf[a:a + cnt], pos0, tab[b], oc.k_scale)
+        O.fp8_group_scales(vf[a:a + cnt], pos0, tab[b], oc.v_scale)
+
+    for b in range(B):                        # prompts: whole-prompt scale calls, then append
+        n = prompt[b]
+        grow(b, n)
+        scales(b, 0, 0, n)
+        for g0 in range(0, n, 64):
+            fixing[(b, g0 // 64)] = (g0, min(64, n - g0))
+        a = starts[b]
+        td = torch.from_numpy(tab).to(DEV)
+        lib.kv_append(cache, k[a:a + n].to(DEV), v[a:a + n].to(DEV),
+                      torch.full((n,), b, dtype=torch.int32, device=DEV),
+                      torch.arange(n, dtype=torch.int32, device=DEV), td)
+        O.append_sequence(oc, kf[a:a + n], vf[a:a + n], tab[b], 0)
+
+    gq = torch.Generator().manual_seed(96)
+    saturated = 0
+    for s in range(steps):
+        pos = [prompt[b] + s for b in range(B)]
+        for b in range(B):
+            p = pos[b]
+            grow(b, p + 1)
+            if p % 64 == 0:                   # the token opens a group: its scale alone
+                fixing[(b, p // 64)] = (p, 1)
+                scales(b, p, p, 1)
+            elif p % 16 == 0:                 # it opens another block of its group
+                t0, cnt = fixing[(b, p // 64)]
+                scales(b, t0, t0, cnt)
+        td = torch.from_numpy(tab).to(DEV)
+        rows = [starts[b] + pos[b] for b in range(B)]
+        kn, vn = k[rows].contiguous().to(DEV), v[rows].contiguous().to(DEV)
+        q = torch.randn(B, hq, d, generator=gq).to(torch.bfloat16)
+        lens = torch.tensor([p + 1 for p in pos], dtype=torch.int32, device=DEV)
+        if folded:
+            out, _ = lib.paged_attn_decode_step(cache, kn, vn, q.to(DEV), td, lens)
+        else:
+            lib.kv_append(cache, kn, vn, torch.arange(B, dtype=torch.int32, device=DEV),
+                          torch.tensor(pos, dtype=torch.int32, device=DEV), td)
+            out, _ = lib.paged_attn_decode(cache, q.to(DEV), td, lens)
+        torch.cuda.synchronize()
+        O.append(oc, kf[rows], vf[rows], np.arange(B), np.array(pos), tab)
+        gk, gv = frag_pages_logical(cache.k.cpu().numpy(), cache.v.cpu().numpy(), 1)
+        assert np.array_equal(gk, oc.k) and np.array_equal(gv, oc.v), f"codes, step {s}"
+        assert np.array_equal(cache.k_scale.cpu().numpy().view(np.uint32),
+                              oc.k_scale.view(np.uint32)), f"k scales, step {s}"
+        assert np.array_equal(cache.v_scale.cpu().numpy().view(np.uint32),
+                              oc.v_scale.view(np.uint32)), f"v scales, step {s}"
+        ref = O.decode(oc, bits(q), "bf16", tab, [p + 1 for p in pos])
+        compare_rows(out.float().cpu().numpy(), ref["o"], "e4m3", f"stream step {s}")
+        for b in range(B):                    # tokens that did not fix their group's scale
+            if pos[b] % 64:
+                blk = tab[b, pos[b] // 16]
+                saturated += int(np.isin(oc.k[blk, :, pos[b] % 16], (0x7E, 0xFE)).sum())
+    alloc.close()
+    assert saturated > 0
+    print(f"folded={folded}: {saturated} saturated K codes among the decode tokens")

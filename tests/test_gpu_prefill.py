@@ -211,39 +211,137 @@ def test_prefill_row_equals_decode(lib):
     ("C4_128K", [0, 32767, 32768, 65537, 98303, 131071]),
 ])
 def test_chunked_prefill_sampled(lib, name, rows):
-    """The whole prompt in 4096-token chunks, KV in sequential shards merged by
-    LSE, as bench.py runs it (C4: 32768 tokens, 8192-token shards; C4-128K:
-    131072 tokens, 32768-token shards); sampled rows, including each shard's
-    first and last, are checked against the oracle."""
+    """The whole prompt through bench.py's own chunked pass (bench.prefill_setup
+    + bench.prefill_pass: 4096-token chunks, KV in sequential shards merged by
+    LSE; C4: 32768 tokens, 8192-token shards; C4-128K: 131072 tokens,
+    32768-token shards) over a NaN-poisoned pool; sampled rows, including
+    each shard's first and last, are checked against the oracle."""
+    import bench
+
     cfg = synth.CONFIGS[name]
-    inp = synth.prefill_inputs(cfg, device=DEV)
-    tables, _ = lib.build_tables([cfg.prompt_len], cfg.pool_blocks, inp["free_order"])
-    td = tables.to(DEV)
-    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, 128, "bf16", fill=float("nan"))
-    outs = torch.empty_like(inp["q"])
-    C, S = cfg.chunk, cfg.shard_len
-    for c in range(cfg.num_chunks):
-        a, b = c * C, (c + 1) * C
-        lib.kv_append(cache, inp["k"][a:b], inp["v"][a:b],
-                      torch.zeros(C, dtype=torch.int32, device=DEV),
-                      torch.arange(a, b, dtype=torch.int32, device=DEV), td)
-        q = inp["q"][a:b]
-        shards = [(j * S, min((j + 1) * S, b)) for j in range(b // S + (1 if b % S else 0))]
-        if len(shards) == 1:                     # as bench.py: final form, nothing to merge
-            lib.paged_attn_prefill(cache, q, a, td[0], 0, b, True, out=outs[a:b])
-            continue
-        parts = [lib.paged_attn_prefill(cache, q, a, td[0], s0, s1, True, partial=True)
-                 for s0, s1 in shards]
-        lib.attn_lse_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]),
-                           torch.stack([p[2] for p in parts]), out=outs[a:b], with_state=False)
+    st = bench.prefill_setup(cfg, poison=True)
+    bench.prefill_pass(cfg, st)
     torch.cuda.synchronize()
     rows = np.array(rows)
-    tab = tables.numpy()
+    tab = st["tables"].numpy()
+    inp = st["inp"]
     dcfg = synth.decode_config("o", (cfg.prompt_len,), cfg.hq, cfg.hkv, 128,
                                pool_blocks=cfg.pool_blocks)
     oc = oracle_cache(dcfg, {"k": inp["k"], "v": inp["v"]}, tab)
     qs = bits(inp["q"][torch.from_numpy(rows).to(DEV)])
-    got = outs[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    got = st["out"][torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
     for i, r in enumerate(rows):
         ref = O.prefill(oc, qs[i:i + 1], "bf16", int(r), tab[0], 0, int(r) + 1, True)
         compare_rows(got[i:i + 1], ref["o"], "bf16", f"{name} row {r}")
+
+
+def _f16_rtz(x):
+    """float64 array -> the fp16 value that round-toward-zero gives, as
+    float64 (saturating at +-65504): the documented conversion of V in bf16
+    prefill."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        h = x.astype(np.float16)                          # nearest even (inf beyond range)
+    over = np.abs(h.astype(np.float64)) > np.abs(x)
+    h[over] = np.nextafter(h[over], np.float16(0))        # one step toward zero
+    return h.astype(np.float64)
+
+
+def test_prefill_bf16_v_outside_fp16_range(lib):
+    """bf16 pools: V enters P V as fp16 with round-toward-zero.  kv head 0
+    holds V ~ N(0,1) * 6e4 (about a quarter of the entries beyond 65504,
+    which saturate), kv head 1 V ~ N(0,1) * 1e-6 (fp16 subnormals, truncated to
+    multiples of 2^-24).  Prefill must equal the oracle fed the converted V,
+    within the bf16 bound scaled by V's scale (attention is linear in V); the
+    decode of the last row over the same pool uses V exactly."""
+    n, hq, hkv, d = 300, 8, 2, 128
+    cfg = synth.prefill_config("vrange", n, 4096, 8192, hq, hkv, d, seed_index=58)
+    inp = synth.prefill_inputs(cfg)
+    scales = torch.tensor([6e4, 1e-6]).view(1, hkv, 1)
+    v = (inp["v"].float() * scales).to(torch.bfloat16)
+    tables, _ = lib.build_tables([n], cfg.pool_blocks, inp["free_order"])
+    td = tables.to(DEV)
+    cache = lib.PagedCache.empty(cfg.pool_blocks, hkv, d, "bf16", fill=float("nan"))
+    lib.kv_append(cache, inp["k"].to(DEV), v.to(DEV), torch.zeros(n, dtype=torch.int32, device=DEV),
+                  torch.arange(n, dtype=torch.int32, device=DEV), td)
+    out, _ = lib.paged_attn_prefill(cache, inp["q"].to(DEV), 0, td[0], 0, n, True)
+    torch.cuda.synchronize()
+    tab = tables.numpy()
+    vx = v.double().numpy()
+    conv = _f16_rtz(vx)
+    assert (np.abs(vx[:, 0]) > 65504).mean() > 0.2                  # saturation happens
+    assert np.abs(conv[:, 1] - vx[:, 1]).max() > 0                   # truncation happens
+    assert np.abs(conv - vx).max(initial=0, where=np.abs(vx) <= 65504) < 2 ** -24
+
+    def oracle_over(vvals):
+        oc = O.new_cache(cfg.pool_blocks, hkv, d, "f32")
+        O.append_sequence(oc, inp["k"].float().numpy(), vvals.astype(np.float32), tab[0], 0)
+        return oc
+
+    ref = O.prefill(oracle_over(conv), bits(inp["q"]), "bf16", 0, tab[0], 0, n, True)["o"]
+    exact = O.prefill(oracle_over(vx), bits(inp["q"]), "bf16", 0, tab[0], 0, n, True)["o"]
+    got = out.double().cpu().numpy()
+    G = hq // hkv
+    for g, c in enumerate((6e4, 1e-6)):
+        hs = slice(g * G, (g + 1) * G)
+        r, gg = ref[:, hs], got[:, hs]
+        err = np.maximum(np.abs(gg - r) - np.abs(r) * 2.0 ** -8, 0).max()
+        assert err <= 2e-3 * c, (g, err, 2e-3 * c)
+        rel = (np.abs(gg - r).max(axis=-1) / np.abs(r).max(axis=-1)).max()
+        assert rel <= 1e-2, (g, rel)
+        print(f"kv head {g}: V x {c:g}: max abs err vs converted-V oracle {err:.3e}, row-rel {rel:.2e}; "
+              f"converted vs exact-V oracle differ by {np.abs(r - exact[:, hs]).max():.3e}")
+    # decode of the last row (all n keys) reads V exactly
+    dec, _ = lib.paged_attn_decode(cache, inp["q"][n - 1:n].to(DEV), td[:1],
+                                   torch.tensor([n], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    gd = dec.double().cpu().numpy()[0]
+    for g, c in enumerate((6e4, 1e-6)):
+        hs = slice(g * G, (g + 1) * G)
+        e = exact[n - 1, hs]
+        err = np.maximum(np.abs(gd[hs] - e) - np.abs(e) * 2.0 ** -8, 0).max()
+        assert err <= 2e-3 * c, ("decode", g, err)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+def test_prefill_skips_out_of_pool_pages_like_decode(lib, fmt):
+    """Table entries outside the pool inside the key range (a contract
+    violation whose result the header calls unspecified): prefill masks those
+    pages' keys out of the softmax, as decode skips them, so both give the
+    attention over the remaining keys (checked against the oracle with those
+    keys hidden) and agree with each other on the last row."""
+    from tests.test_gpu_prefill_fp8 import _oracle8, _prompt8
+
+    n = 300
+    if fmt == "bf16":
+        cfg, inp, tables, td, cache = _prompt(lib, n)
+        oc = _oracle(cfg, inp, tables, cfg.hkv)
+    else:
+        cfg, inp, tables, td, cache = _prompt8(lib, n)
+        oc = _oracle8(cfg, inp, tables)
+    bad = tables.copy()
+    bad[0, 5] = cfg.pool_blocks + 7            # tokens 80..95
+    bad[0, 12] = -3                            # tokens 192..207
+    bad_d = torch.from_numpy(bad).to(DEV)
+    out, _ = lib.paged_attn_prefill(cache, inp["q"].to(DEV), 0, bad_d[0], 0, n, True)
+    torch.cuda.synchronize()
+    hidden = np.zeros(n, dtype=bool)
+    hidden[80:96] = hidden[192:208] = True
+    t = np.arange(n)
+    vis = (t[None, :] <= t[:, None]) & ~hidden[None, :]
+    q = O.bf16_bits_to_f64(bits(inp["q"]))
+    G = cfg.hq // cfg.hkv
+    ref = np.zeros((n, cfg.hq, cfg.head_dim))
+    for g in range(cfg.hkv):
+        K, V = O.gather_kv(oc, tables[0], n, g)
+        for h in range(g * G, (g + 1) * G):
+            ref[:, h] = O.attend(q[:, h], K, V, vis, 1.0 / np.sqrt(cfg.head_dim))[0]
+    compare_rows(out.float().cpu().numpy(), ref, "bf16" if fmt == "bf16" else "e4m3",
+                 f"{fmt} prefill with out-of-pool pages")
+    dec, _ = lib.paged_attn_decode(cache, inp["q"][n - 1:n].to(DEV), bad_d,
+                                   torch.tensor([n], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    compare_rows(dec.float().cpu().numpy(), ref[n - 1:n], "bf16" if fmt == "bf16" else "e4m3",
+                 f"{fmt} decode with out-of-pool pages")
+    diff = (out[n - 1].float() - dec[0].float()).abs().max().item()
+    assert diff <= 8e-3, diff

@@ -610,3 +610,140 @@ def test_published_prefix_leaves_index_when_freed():
     alloc.release(6)
     assert not alloc.by_hash and alloc.free_count() == 8
     assert alloc.match_prefix(7, hs) == 0
+
+
+# ---------------------------------------------------------------- KV offload
+def _read_back(alloc, dev, host, seq, n):
+    """Token values of sequence `seq` ([n]) read through its page table: from
+    the device pool for resident blocks, from its host slot otherwise."""
+    out = []
+    for j in range(-(-n // 16)):
+        b, slot, _ = alloc.block_state(seq, j)
+        pool, blk = (host, slot) if b == O.OFFLOADED else (dev, b)
+        cnt = min(16, n - 16 * j)
+        out.extend(pool.k[blk, 0, :cnt, 0].tolist())
+    return out
+
+
+def test_offload_page_table_keeps_every_sequence_its_own_tokens():
+    """Brute force against the plain definition with a host tier [P3 section
+    4.2]: every sequence owns its list of token values; blocks move between the
+    device pool and host slots (O.copy_blocks over the returned pairs), grow,
+    fork, publish / match prefixes and release in random order, and after
+    every step each sequence reads back exactly its own tokens through its page
+    table; device blocks and host slots are each held once or free."""
+    nb, nh = 40, 24
+    alloc = O.Allocator(nb, synth.free_order(nb, 41).numpy())
+    alloc.set_host_slots(nh)
+    dev = O.new_cache(nb, 1, 4, "f32", fill=np.nan)
+    host = O.new_cache(nh, 1, 4, "f32", fill=np.nan)
+    truth = {}
+    r = np.random.default_rng(11)
+    nxt = [1.0]
+    moved = {"out": 0, "in": 0}
+    for step in range(2000):
+        op = r.random()
+        seqs = sorted(truth)
+        if op < 0.3 or not seqs:                           # grow
+            s = int(r.integers(0, 6))
+            old = truth.get(s, [])
+            toks = [nxt[0] + i for i in range(int(r.integers(1, 24)))]
+            try:
+                table, pair = alloc.reserve_cow(s, len(old) + len(toks))
+            except (O.OutOfBlocks, O.Offloaded):
+                continue
+            nxt[0] += len(toks)
+            if pair is not None:
+                O.copy_blocks(dev, dev, [pair[0]], [pair[1]])
+            vals = np.array(toks, np.float32)[:, None, None] * np.ones((1, 1, 4), np.float32)
+            O.append(dev, vals, vals, np.zeros(len(toks), np.int32),
+                     np.arange(len(old), len(old) + len(toks)), np.array([table], np.int32))
+            truth[s] = old + toks
+        elif op < 0.5:                                     # offload a range
+            s = seqs[int(r.integers(0, len(seqs)))]
+            first, count = int(r.integers(0, 6)), int(r.integers(0, 6))
+            try:
+                pairs = alloc.offload(s, first, count)
+            except (O.OutOfBlocks, O.SharedBlock):
+                continue
+            O.copy_blocks(dev, host, [p[0] for p in pairs], [p[1] for p in pairs])
+            moved["out"] += len(pairs)
+        elif op < 0.7:                                     # page a range back in
+            s = seqs[int(r.integers(0, len(seqs)))]
+            first, count = int(r.integers(0, 6)), int(r.integers(0, 6))
+            try:
+                pairs = alloc.page_in(s, first, count)
+            except O.OutOfBlocks:
+                continue
+            O.copy_blocks(host, dev, [p[0] for p in pairs], [p[1] for p in pairs])
+            moved["in"] += len(pairs)
+        elif op < 0.78:                                    # fork
+            s = seqs[int(r.integers(0, len(seqs)))]
+            d = int(r.integers(0, 6))
+            if d in truth:
+                continue
+            try:
+                alloc.fork(s, d)
+            except O.Offloaded:
+                assert O.OFFLOADED in alloc.tables[s]
+                continue
+            truth[d] = list(truth[s])
+        elif op < 0.86:                                    # publish, then a new one matches
+            s = seqs[int(r.integers(0, len(seqs)))]
+            alloc.publish_prefix(s, _chain_hashes(truth[s]))
+            d = int(r.integers(0, 6))
+            if d not in truth:
+                m = alloc.match_prefix(d, _chain_hashes(truth[s]))
+                truth[d] = truth[s][:16 * m]
+        else:                                              # release
+            s = seqs[int(r.integers(0, len(seqs)))]
+            alloc.release(s)
+            del truth[s]
+        # invariants: device blocks held or free, host slots used or free, once each
+        held, slots = {}, []
+        for s, t in alloc.tables.items():
+            for j, b in enumerate(t):
+                if b == O.OFFLOADED:
+                    slots.append(alloc.slot_of[s][j])
+                else:
+                    assert alloc.slot_of[s][j] == -1
+                    held[b] = held.get(b, 0) + 1
+        assert all(alloc.refcount(b) == held.get(b, 0) for b in range(nb))
+        assert sorted(list(held) + alloc.free) == list(range(nb))
+        assert sorted(slots + alloc.host_free) == list(range(nh))
+        assert all(h not in alloc.hash_of or True for h in slots)
+        assert all(b in held for b in alloc.hash_of)
+        for s, toks in truth.items():
+            assert _read_back(alloc, dev, host, s, len(toks)) == toks, (step, s)
+    assert moved["out"] > 50 and moved["in"] > 20
+
+
+def test_offload_refusals_and_coldest_order():
+    alloc = O.Allocator(8)
+    alloc.set_host_slots(3)
+    alloc.reserve(0, 40)                        # blocks 0, 1, 2 (the last partly filled)
+    assert alloc.offload(0, 2, 1) == [(2, 0)]
+    assert alloc.table(0) == [0, 1, O.OFFLOADED] and alloc.block_state(0, 2) == (O.OFFLOADED, 0, -1)
+    for n in (41, 48):                          # the growth would write into host memory
+        with pytest.raises(O.Offloaded):
+            alloc.reserve(0, n)
+    assert alloc.lens[0] == 40 and alloc.reserve(0, 40) == [0, 1, O.OFFLOADED]
+    with pytest.raises(O.Offloaded):            # host slots are not shared
+        alloc.fork(0, 1)
+    assert alloc.page_in(0, 0, 8) == [(0, 3)]   # the free list's front: block 3
+    alloc.fork(0, 1)
+    with pytest.raises(O.SharedBlock):          # shared blocks stay on the device
+        alloc.offload(0, 0, 1)
+    alloc.release(1)
+    assert alloc.reserve(2, 64) == [4, 5, 6, 7]
+    with pytest.raises(O.OutOfBlocks):          # 4 blocks, 3 free host slots: nothing moves
+        alloc.offload(2, 0, 4)
+    assert O.OFFLOADED not in alloc.table(2) and alloc.host_free_count() == 3
+    alloc.touch(0, 0, 3, 7)
+    alloc.touch(2, 1, 2, 3)
+    alloc.touch(2, 0, 1, 9)
+    # candidates: full, resident blocks held by one table (seq 0's partly
+    # filled third block is not one); never read (-1) first, then by step
+    assert alloc.coldest(10) == [(2, 3), (2, 1), (2, 2), (0, 0), (0, 1), (2, 0)]
+    assert alloc.coldest(2) == [(2, 3), (2, 1)]
+    assert alloc.block_state(2, 0) == (4, -1, 9)
