@@ -160,7 +160,10 @@ def bench_decode(cfg, steps, warmup, partition_blocks=0):
     return ms_step, ms_dec, ms_merge, st
 
 
-def decode_record(cfg, steps, warmup, partition_blocks):
+def decode_record(cfg, steps, warmup, partition_blocks, keep_rows=None):
+    """Timed decode steps of one workload; returns (record, GPU output of the
+    rows in keep_rows as float64 [len(keep_rows), Hq, d] on the host)."""
+    import torch
     from paged_kv_cache_210_amd import accounting as A
 
     ms_step, ms_dec, ms_merge, st = bench_decode(cfg, steps, warmup, partition_blocks)
@@ -179,36 +182,93 @@ def decode_record(cfg, steps, warmup, partition_blocks):
         "merge_ms": ms_merge,
         "ms_per_step_no_events": st["ms_per_step_no_events"],
         "partitions": st["partitions"],
+        "partition_blocks": partition_blocks,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": A.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / A.HBM_PEAK_GBS, "traffic": measured_traffic(cfg),
                      "kernel": ("decode_mfma_kernel with the append folded in "
                                 "(pkv_paged_attn_decode_step_partial)" if st["folded"] else
                                 "decode_mfma_kernel (pkv_paged_attn_decode_partial)"),
                      "ms_per_launch": ms_dec, "ms_per_launch_median": st["decode_ms_median"],
-                     "ms_per_launch_min": st["decode_ms_min"], "bytes_per_launch": kbytes},
+                     "ms_per_launch_min": st["decode_ms_min"], "bytes_per_launch": kbytes,
+                     "clock_ghz_observed": observed_clock(_key(cfg))},
     }
-    return rec, st
+    rows = None
+    if keep_rows is not None:
+        rows = st["out"][list(keep_rows)].double().cpu().numpy()
+    del st
+    torch.cuda.empty_cache()
+    return rec, rows
+
+
+def _key(cfg):
+    """The workload's name in synth.CONFIGS (C2, C3, C4_128K, ...)."""
+    import synth
+
+    return next((k for k, c in synth.CONFIGS.items() if c == cfg), cfg.name)
+
+
+def _gated(path, key):
+    """A committed counter figure, or None when a kernel source it was taken
+    with has changed since (each record stores the sha256 of its sources)."""
+    import hashlib
+
+    try:
+        rec = json.load(open(os.path.join(ROOT, path)))
+        w = rec["workloads"][key]
+        shas = dict(rec.get("kernel_source_sha256", {}))
+        shas.update(w.get("kernel_source_sha256", {}))
+        for src, sha in shas.items():
+            if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != sha:
+                return None
+        return w
+    except (OSError, KeyError, ValueError, TypeError, AttributeError):
+        return None
 
 
 def measured_traffic(cfg):
     """HBM bytes per launch of the decode kernel from the committed counter
     runs (profiles/decode_hbm_traffic.json), or None when the kernel source has
     changed since they were taken."""
-    import hashlib
-
-    path = os.path.join(ROOT, "profiles", "decode_hbm_traffic.json")
-    src = os.path.join(ROOT, "paged_kv_cache_210_amd", "csrc", "decode.hip")
-    key = {"C2": "C2", "C3": "C3", "C5": "C5"}.get(cfg.name.split()[0])
-    try:
-        rec = json.load(open(path))
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha256"]:
-            return None
-        return rec["workloads"][key]["traffic_bytes"]
-    except (OSError, KeyError, ValueError):
-        return None
+    w = _gated("profiles/decode_hbm_traffic.json", _key(cfg))
+    return None if w is None else w["traffic_bytes"]
 
 
-def _prefill_setup(cfg):
+def prefill_traffic(cfg):
+    """HBM bytes per prompt of the prefill kernel launches from the committed
+    FETCH_SIZE / WRITE_SIZE runs (profiles/prefill_hbm_traffic.json), or None
+    when the kernel source has changed since."""
+    w = _gated("profiles/prefill_hbm_traffic.json", _key(cfg))
+    return None if w is None else w["traffic_bytes_per_prompt"]
+
+
+def observed_clock(key):
+    """Average shader clock over the dominant kernel's launches (GPU-active
+    cycles per XCD from GRBM_GUI_ACTIVE over the traced kernel time) from the
+    committed counter run (profiles/observed_clock.json), or None when the
+    kernel source has changed since."""
+    w = _gated("profiles/observed_clock.json", key)
+    return None if w is None else w["clock_ghz"]
+
+
+def chunk_plan(cfg):
+    """The chunked pass over a prompt: for each 4096-token (cfg.chunk) query
+    chunk c, rows [a, b), the KV shard ranges it attends to, in order.  Shards
+    are the contiguous cfg.shard_len-token ranges of the keys written so far
+    (the chunk's own included); a chunk that sees one shard only is attended
+    in the final form, the others as one partial per shard merged by LSE."""
+    C, S = cfg.chunk, cfg.shard_len
+    plan = []
+    for c in range(cfg.num_chunks):
+        a, b = c * C, min((c + 1) * C, cfg.prompt_len)
+        shards = [(j * S, min((j + 1) * S, b)) for j in range(-(-b // S))]
+        plan.append((c, a, b, shards))
+    return plan
+
+
+def prefill_setup(cfg, poison=False):
+    """Device state of one prompt: inputs drawn on the GPU, the table from the
+    library allocator, an empty pool (NaN / 0x7F codes when poison), shard
+    partial buffers and the output."""
     import torch
     from paged_kv_cache_210_amd import lib
     import synth
@@ -217,7 +277,11 @@ def _prefill_setup(cfg):
     inp = synth.prefill_inputs(cfg, device=dev)
     tables, _ = lib.build_tables([cfg.prompt_len], cfg.pool_blocks, inp["free_order"])
     td = tables.to(dev)
-    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, cfg.kv_dtype, device=dev)
+    fill = None
+    if poison:
+        fill = 0x7F if cfg.kv_dtype == "e4m3" else float("nan")
+    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, cfg.head_dim, cfg.kv_dtype, device=dev,
+                                 fill=fill)
     C, S = cfg.chunk, cfg.shard_len
     max_parts = -(-cfg.prompt_len // S)
     part = (torch.empty(max_parts, C, cfg.hq, cfg.head_dim, dtype=torch.float32, device=dev),
@@ -228,51 +292,50 @@ def _prefill_setup(cfg):
     pos = torch.arange(cfg.prompt_len, dtype=torch.int32, device=dev)
     seq = torch.zeros(C, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
-    return dict(inp=inp, td=td, cache=cache, part=part, out=out, lse1=lse1, pos=pos, seq=seq)
+    return dict(inp=inp, tables=tables, td=td, cache=cache, part=part, out=out, lse1=lse1,
+                pos=pos, seq=seq)
 
 
 def prefill_pass(cfg, st, ev=None):
-    """One chunked pass over the prompt: per chunk append its K/V (for an E4M3
-    pool: first the chunk's 64-token group scales), attend to each visible KV
-    shard (partial form), merge the shards by LSE; a chunk that sees a single
-    shard is attended in the final form, with nothing to merge."""
+    """One chunked pass over the prompt (chunk_plan): per chunk append its K/V
+    (for an E4M3 pool: first the chunk's 64-token group scales), then attend
+    to its shards and merge them by LSE into st["out"]."""
     from paged_kv_cache_210_amd import lib
 
-    C, S = cfg.chunk, cfg.shard_len
     inp, td, cache, (po, pm, pl) = st["inp"], st["td"], st["cache"], st["part"]
-    for c in range(cfg.num_chunks):
-        a, b = c * C, min((c + 1) * C, cfg.prompt_len)
+    for c, a, b, shards in chunk_plan(cfg):
         if ev is not None:
             ev.append(("append", c))
         if cfg.kv_dtype == "e4m3":
             lib.fp8_group_scales(cache, inp["k"][a:b], inp["v"][a:b], a, td[0])
         lib.kv_append(cache, inp["k"][a:b], inp["v"][a:b], st["seq"][:b - a], st["pos"][a:b], td)
         q = inp["q"][a:b]
-        nsh = -(-b // S)
         if ev is not None:
             ev.append(("start", c))
-        if nsh == 1:          # one shard holds every visible key: nothing to merge
-            lib.paged_attn_prefill(cache, q, a, td[0], 0, b, True, out=st["out"][a:b],
+        if len(shards) == 1:          # one shard holds every visible key: nothing to merge
+            lo, hi = shards[0]
+            lib.paged_attn_prefill(cache, q, a, td[0], lo, hi, True, out=st["out"][a:b],
                                    out_lse=st["lse1"][:b - a])
         else:
-            for j in range(nsh):
-                lib.paged_attn_prefill(cache, q, a, td[0], j * S, min((j + 1) * S, b), True,
-                                       partial=True,
+            for j, (lo, hi) in enumerate(shards):
+                lib.paged_attn_prefill(cache, q, a, td[0], lo, hi, True, partial=True,
                                        part=(po[j, :b - a], pm[j, :b - a], pl[j, :b - a]))
-            lib.attn_lse_merge(po[:nsh, :b - a], pm[:nsh, :b - a], pl[:nsh, :b - a],
+            n = len(shards)
+            lib.attn_lse_merge(po[:n, :b - a], pm[:n, :b - a], pl[:n, :b - a],
                                out=st["out"][a:b], with_state=False)
         if ev is not None:
             ev.append(("end", c))
 
 
-def prefill_record(cfg, reps):
+def prefill_record(cfg, reps, keep_rows=None):
+    """Timed chunked passes over one prompt; returns (record, GPU output rows
+    keep_rows as float64 on the host)."""
     import torch
     from paged_kv_cache_210_amd import accounting as A
 
-    st = _prefill_setup(cfg)
+    st = prefill_setup(cfg)
     prefill_pass(cfg, st)                      # warm-up pass
     torch.cuda.synchronize()
-    marks = []
     events = {}
 
     class _Ev(list):
@@ -301,9 +364,12 @@ def prefill_record(cfg, reps):
     abytes = A.append_bytes(cfg.prompt_len, cfg.hkv, cfg.head_dim, cfg.kv_dtype)
     flops = A.causal_prompt_flops(cfg.prompt_len, cfg.hq, cfg.head_dim)
     tflops = flops / (attn_ms * 1e-3) / 1e12
+    rows = None
+    if keep_rows is not None:
+        rows = st["out"][torch.tensor(list(keep_rows), device="cuda")].double().cpu().numpy()
     del st
     torch.cuda.empty_cache()
-    return {
+    rec = {
         "workload": cfg.name,
         "prompt_tok_per_s": cfg.prompt_len / (total_ms * 1e-3),
         "ms_per_prompt": total_ms,
@@ -311,11 +377,13 @@ def prefill_record(cfg, reps):
         "tflops": tflops,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": A.BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / A.BF16_MFMA_PEAK_TFLOPS,
-                     "traffic": None,
+                     "traffic": prefill_traffic(cfg),
+                     "traffic_unit": "HBM bytes per prompt, prefill_kernel launches",
                      "kernel": "pkv_paged_attn_prefill (all shards) + pkv_attn_lse_merge",
                      "mfma": ("fp16 x fp16 (E4M3 tiles dequantised to fp16, q converted)"
                               if cfg.kv_dtype == "e4m3" else "bf16 (K Q^T), fp16 (P V)"),
-                     "flops_per_prompt": flops},
+                     "flops_per_prompt": flops,
+                     "clock_ghz_observed": observed_clock(_key(cfg))},
         "kv_dtype": cfg.kv_dtype,
         "kv_append": {"ms_per_prompt": append_ms, "bytes_per_prompt": abytes,
                       "includes": "kv_append" + (" + fp8_group_scales (scales read the chunk once "
@@ -324,6 +392,7 @@ def prefill_record(cfg, reps):
                       "gbs": abytes / (append_ms * 1e-3) / 1e9,
                       "frac_of_hbm_peak": abytes / (append_ms * 1e-3) / 1e9 / A.HBM_PEAK_GBS},
     }
+    return rec, rows
 
 
 def block_copy_record(reps=5, blocks=8192, cow_blocks=32):
@@ -403,113 +472,244 @@ def hbm_copy_record(reps=20, nbytes=1 << 30):
             "bytes_written": nbytes, "ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
-def cpu_baseline_decode(cfg, budget_s):
+# ---------------------------------------------------------------- oracle baselines
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+def oracle_error(got, ref):
+    """Error of bf16 GPU outputs against the oracle on the same rows:
+    max |got - ref|, the same beyond the output's own rounding (half a bf16 ulp
+    of ref), and the per-row inf-norm relative error (max over rows of
+    max_i |got_i - ref_i| / max_i |ref_i|), rows being the last axis."""
+    import numpy as np
+
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    diff = np.abs(got - ref)
+    a = np.abs(ref)
+    half_ulp = np.where(a > 0, 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))) - 8), 0.0)
+    den = a.max(axis=-1)
+    live = den > 0
+    rel = (diff.max(axis=-1)[live] / den[live]).max() if live.any() else 0.0
+    return {"max_abs": float(diff.max()),
+            "max_abs_beyond_bf16_rounding": float(np.maximum(diff - half_ulp, 0).max()),
+            "row_rel": float(rel), "rows": int(np.prod(got.shape[:-1]))}
+
+
+def _kv_host(t, fmt):
+    """Source K/V rows (device tensor) -> what the oracle's append takes."""
+    import numpy as np
+    import torch
+
+    if fmt == "e4m3":
+        return t.float().cpu().numpy()
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_baseline_decode(cfg, budget_s, gpu_rows=None, seqs=None, kv_heads=None,
+                        piece=1 << 16):
     """The fp64 oracle, as it stands, on a bounded sample of the same decode
-    step: append the newest token of each sampled sequence, then attention over
-    all its keys.  Sequences are added until the budget is used; when the whole
-    batch takes less, the steps are repeated over the batch (re-appending a
-    token writes the same slot with the same values) until it is used."""
+    step: for each sampled sequence, append its newest token, then attention
+    of its query over all its keys, for the query heads of the sampled kv
+    heads (all by default).  Sequences are taken in turn, and the turns
+    repeated (re-appending a token writes the same slot with the same values)
+    until the CPU budget is used.  With kv_heads sampled, a step does that
+    fraction of a token's work, so the rate is scaled by it (tokens/s =
+    steps * len(kv_heads) / Hkv / time).  The sampled outputs are compared
+    with the GPU's (gpu_rows [len(seqs), Hq, d], in the order of seqs)."""
     import numpy as np
     import torch
     from oracle import pkv_oracle as O
     import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        blas_threads = 1
+    seqs = list(range(cfg.batch)) if seqs is None else list(seqs)
+    heads = list(range(cfg.hkv)) if kv_heads is None else list(kv_heads)
+    G = cfg.hq // cfg.hkv
+    qheads = [g * G + i for g in heads for i in range(G)]
     inp = synth.decode_inputs(cfg, device="cuda")
-    order = inp["free_order"].numpy()
-    tables, _ = O.build_tables(cfg.seq_lens, cfg.pool_blocks, order)
-
-    def bits(t):
-        return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-
+    tables, _ = O.build_tables(cfg.seq_lens, cfg.pool_blocks, inp["free_order"].numpy())
     cache = O.new_cache(cfg.pool_blocks, cfg.hkv, cfg.head_dim, cfg.kv_dtype)
-    q = bits(inp["q"])
-    done, spent = 0, 0.0
-    start = 0
-    newest = []
-
-    def timed_step(b, n, kn, vn):
-        t0 = time.perf_counter()
-        O.append(cache, kn, vn, np.array([b], np.int32), np.array([n - 1], np.int32), tables)
-        O.decode(cache, q[b:b + 1], "bf16", tables[b:b + 1], [n])
-        return time.perf_counter() - t0
-
-    for b, n in enumerate(cfg.seq_lens):
-        k = bits(inp["k"][start:start + n])
-        v = bits(inp["v"][start:start + n])
-        O.append_sequence(cache, k[:n - 1], v[:n - 1], tables[b], 0)        # untimed pre-fill
-        newest.append((k[n - 1:n], v[n - 1:n]))
-        spent += timed_step(b, n, *newest[b])
-        done += 1
-        start += n
-        if spent >= budget_s:
-            break
-    passes = 1
-    while spent < budget_s and done == passes * cfg.batch:
-        for b, n in enumerate(cfg.seq_lens):
-            spent += timed_step(b, n, *newest[b])
+    q = inp["q"].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    starts = np.concatenate([[0], np.cumsum(cfg.seq_lens)[:-1]])
+    newest = {}
+    setup0 = time.perf_counter()
+    for b in seqs:                                     # untimed: the pool before the step
+        n, a = cfg.seq_lens[b], int(starts[b])
+        for p0 in range(0, n, piece):
+            p1 = min(n, p0 + piece)
+            k = _kv_host(inp["k"][a + p0:a + p1], cfg.kv_dtype)
+            v = _kv_host(inp["v"][a + p0:a + p1], cfg.kv_dtype)
+            if cfg.kv_dtype == "e4m3":                 # scales from every token, newest included
+                O.fp8_group_scales(k, p0, tables[b], cache.k_scale)
+                O.fp8_group_scales(v, p0, tables[b], cache.v_scale)
+            m = min(p1, n - 1) - p0
+            if m > 0:
+                O.append_sequence(cache, k[:m], v[:m], tables[b], p0, heads=heads)
+            if p1 == n:
+                newest[b] = (k[n - 1 - p0:n - p0], v[n - 1 - p0:n - p0])
+    setup_s = time.perf_counter() - setup0
+    del inp
+    done, spent, outs = 0, 0.0, {}
+    while spent < budget_s:
+        for b in seqs:
+            n = cfg.seq_lens[b]
+            t0 = time.perf_counter()
+            O.append(cache, newest[b][0], newest[b][1], np.array([b], np.int32),
+                     np.array([n - 1], np.int32), tables)
+            r = O.decode(cache, q[b:b + 1], cfg.q_dtype, tables[b:b + 1], [n],
+                         kv_heads=None if kv_heads is None else heads)
+            spent += time.perf_counter() - t0
+            outs[b] = r["o"][0][qheads]
             done += 1
             if spent >= budget_s:
                 break
-        passes += 1
-    seqs = min(done, cfg.batch)
-    return {"value": done / spent, "unit": "tok/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{done} decode steps over {seqs} of {cfg.batch} sequences of {cfg.name} "
-                      f"(append newest token + decode over {cfg.seq_lens[0]} keys, all "
-                      f"{cfg.hq} heads), {spent:.1f} s of CPU time",
-            "host_cpus": len(os.sched_getaffinity(0))}
+    frac = len(heads) / cfg.hkv
+    what = (f"all {cfg.hq} heads" if frac == 1 else
+            f"the {len(qheads)} query heads of kv head(s) {heads}, i.e. {frac:g} of a token's "
+            f"work per step, rate scaled by that fraction")
+    rec = {"value": done * frac / spent, "unit": "tok/s", "cores": int(_threads()),
+           "kind": "oracle",
+           "sample": f"{done} decode steps (append the newest token, attend over all "
+                     f"{cfg.seq_lens[seqs[0]]} keys, {what}) taking turns over "
+                     f"{len(seqs)} of {cfg.batch} sequences of {cfg.name}, {spent:.1f} s of "
+                     f"CPU time (+{setup_s:.1f} s untimed to fill the oracle pool)",
+           "host_cpus": len(os.sched_getaffinity(0))}
+    if gpu_rows is not None:
+        got = [gpu_rows[i][qheads] for i, b in enumerate(seqs) if b in outs]
+        want = [outs[b] for b in seqs if b in outs]
+        rec["gpu_error_vs_oracle"] = oracle_error(np.stack(got), np.stack(want))
+        rec["gpu_error_vs_oracle"]["sequences"] = [b for b in seqs if b in outs]
+        rec["gpu_error_vs_oracle"]["q_heads"] = "all" if frac == 1 else qheads
+    return rec
 
 
-def cpu_baseline_prefill(cfg, budget_s, device="cuda"):
+def cpu_baseline_prefill(cfg, budget_s, gpu_rows=None, edge_rows=()):
     """The fp64 oracle, as it stands, on a bounded sample of the same causal
     prefill: query rows taken from the end of the prompt (the longest ones),
-    each against all of its visible keys, all heads.  The rate is attention
-    flops (4*d per visible key per head) per second, the same unit as the GPU
-    figure; the prompt's KV is put into the oracle pool untimed."""
+    each against all of its visible keys, all heads, timed until the CPU
+    budget is used; the rate is attention flops (4*d per visible key per head)
+    per second, the GPU figure's unit.  The prompt's KV is put into the oracle
+    pool untimed (E4M3: scales per chunk, as the GPU pass makes them).  The
+    timed rows and the untimed edge_rows are compared with the GPU's output
+    (gpu_rows: the rows of prefill_rows(cfg, edge_rows), in order)."""
     import numpy as np
     import torch
     from oracle import pkv_oracle as O
     import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        blas_threads = 1
-    inp = synth.prefill_inputs(cfg, device=device)
+    inp = synth.prefill_inputs(cfg, device="cuda")
     tables, _ = O.build_tables([cfg.prompt_len], cfg.pool_blocks, inp["free_order"].numpy())
-
-    def bits(t):
-        return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-
-    cache = O.new_cache(cfg.pool_blocks, cfg.hkv, cfg.head_dim, "bf16")
-    O.append_sequence(cache, bits(inp["k"]), bits(inp["v"]), tables[0], 0)   # untimed
-    q = bits(inp["q"])
-    rows, pairs, spent = 0, 0, 0.0
+    cache = O.new_cache(cfg.pool_blocks, cfg.hkv, cfg.head_dim, cfg.kv_dtype)
+    setup0 = time.perf_counter()
+    for c, a, b, _ in chunk_plan(cfg):
+        k = _kv_host(inp["k"][a:b], cfg.kv_dtype)
+        v = _kv_host(inp["v"][a:b], cfg.kv_dtype)
+        if cfg.kv_dtype == "e4m3":
+            O.fp8_group_scales(k, a, tables[0], cache.k_scale)
+            O.fp8_group_scales(v, a, tables[0], cache.v_scale)
+        O.append_sequence(cache, k, v, tables[0], a)
+    q = inp["q"].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    setup_s = time.perf_counter() - setup0
+    del inp
+    got_rows, outs, pairs, spent = [], {}, 0, 0.0
     for r in range(cfg.prompt_len - 1, -1, -1):
         t0 = time.perf_counter()
-        O.prefill(cache, q[r:r + 1], "bf16", r, tables[0], 0, r + 1, True)
+        res = O.prefill(cache, q[r:r + 1], "bf16", r, tables[0], 0, r + 1, True)
         spent += time.perf_counter() - t0
-        rows += 1
+        outs[r] = res["o"][0]
         pairs += r + 1
         if spent >= budget_s:
             break
+    timed_rows = sorted(outs)
+    for r in edge_rows:                              # untimed rows for the error only
+        if r not in outs:
+            outs[r] = O.prefill(cache, q[r:r + 1], "bf16", r, tables[0], 0, r + 1, True)["o"][0]
     flops = 4 * cfg.head_dim * cfg.hq * pairs
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"{rows} query rows (the last ones) of {cfg.name}, each against all its "
-                      f"visible keys, all {cfg.hq} heads, {spent:.1f} s of CPU time",
-            "host_cpus": len(os.sched_getaffinity(0))}
+    rec = {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(_threads()),
+           "kind": "oracle",
+           "sample": f"{len(timed_rows)} query rows (the last ones) of {cfg.name}, each against "
+                     f"all its visible keys, all {cfg.hq} heads, {spent:.1f} s of CPU time "
+                     f"(+{setup_s:.1f} s untimed to fill the oracle pool)",
+           "host_cpus": len(os.sched_getaffinity(0)), "timed_rows": len(timed_rows)}
+    if gpu_rows is not None:
+        rows = prefill_rows(cfg, edge_rows)
+        sel = [i for i, r in enumerate(rows) if r in outs]
+        rec["gpu_error_vs_oracle"] = oracle_error(gpu_rows[sel],
+                                                  np.stack([outs[rows[i]] for i in sel]))
+        rec["gpu_error_vs_oracle"]["query_rows"] = [rows[i] for i in sel]
+    return rec
+
+
+def prefill_rows(cfg, edge_rows, n_tail=64):
+    """Rows whose GPU output is kept for the oracle comparison: the edge rows
+    and the last n_tail rows of the prompt (more than the oracle's budget
+    reaches: the comparison takes those it computed)."""
+    tail = list(range(cfg.prompt_len - n_tail, cfg.prompt_len))
+    return sorted(set(list(edge_rows) + tail))
+
+
+def edge_rows_of(cfg):
+    """First rows, the ends of the first chunk and of every shard."""
+    rows = {0, 1, 63, 64, cfg.chunk - 1, cfg.chunk}
+    for j in range(1, cfg.num_shards):
+        rows |= {j * cfg.shard_len - 1, j * cfg.shard_len}
+    return sorted(r for r in rows if r < cfg.prompt_len)
 
 
 # Blocks per decode partition: the 131072-token workload is defined with
 # 256-block partitions; the others use the library's choice (0), which for the
 # 1M-token workload is 128 partitions of 512 blocks (1024 workgroups).
 PARTITION_BLOCKS = {"C2": 0, "C3": 256, "C5": 0}
+# Sequences (and, for the 1M-token workload, kv heads: filling the oracle's
+# E4M3 pool for all 8 would take minutes) whose output the oracle recomputes.
+ORACLE_SEQS = {"C2": None, "C3": [0, 1, 2, 3], "C5": [0]}
+ORACLE_KV_HEADS = {"C2": None, "C3": None, "C5": [3]}
+# CPU seconds of each oracle baseline, as fractions of --cpu-seconds.
+CPU_SHARE = {"C2": 0.5, "C3": 0.6, "C5": 0.8, "C4": 0.4, "C4_128K": 0.6, "C4_FP8": 0.4}
+
+
+def decode_with_baseline(name, args):
+    import synth
+
+    c = synth.CONFIGS[name]
+    seqs = ORACLE_SEQS[name]
+    keep = list(range(c.batch)) if seqs is None else seqs
+    _log(f"[bench] decode {c.name}")
+    rec, rows = decode_record(c, args.steps, args.warmup, PARTITION_BLOCKS[name], keep_rows=keep)
+    _log(f"[bench]   {rec['tok_per_s']:.0f} tok/s, decode {rec['roofline']['achieved']:.0f} GB/s")
+    if not args.no_cpu_baseline:
+        _log(f"[bench]   oracle baseline {name}")
+        rec["cpu_baseline"] = cpu_baseline_decode(c, args.cpu_seconds * CPU_SHARE[name], rows,
+                                                  seqs=keep, kv_heads=ORACLE_KV_HEADS[name])
+        rec["cpu_baseline"]["gpu_speedup"] = rec["tok_per_s"] / rec["cpu_baseline"]["value"]
+        _log(f"[bench]   oracle {rec['cpu_baseline']['value']:.3g} tok/s; GPU error "
+             f"{rec['cpu_baseline'].get('gpu_error_vs_oracle')}")
+    return rec
+
+
+def prefill_with_baseline(name, args):
+    import synth
+
+    c = synth.CONFIGS[name]
+    edges = edge_rows_of(c)
+    keep = prefill_rows(c, edges)
+    _log(f"[bench] prefill {c.name}")
+    rec, rows = prefill_record(c, args.prefill_reps, keep_rows=keep)
+    _log(f"[bench]   {rec['tflops']:.0f} TFLOP/s, {rec['ms_per_prompt']:.2f} ms/prompt; "
+         f"kv_append {rec['kv_append']['gbs']:.0f} GB/s")
+    if not args.no_cpu_baseline:
+        _log(f"[bench]   oracle baseline {name}")
+        rec["cpu_baseline"] = cpu_baseline_prefill(c, args.cpu_seconds * CPU_SHARE[name], rows,
+                                                   edge_rows=edges)
+        rec["cpu_baseline"]["gpu_speedup"] = rec["tflops"] / rec["cpu_baseline"]["value"]
+        _log(f"[bench]   oracle {rec['cpu_baseline']['value']:.3g} TFLOP/s; GPU error "
+             f"{rec['cpu_baseline'].get('gpu_error_vs_oracle')}")
+    return rec
 
 
 def main(argv=None):
@@ -517,12 +717,13 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
+    ap.add_argument("--no-secondary", action="store_true", help="headline workloads only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU budget unit of the oracle baselines (each takes a share)")
     ap.add_argument("--only", choices=["C2", "C3", "C5", "C4", "C4_128K", "C4_FP8", "hbm_copy",
                                        "block_copy"],
-                    help="run one workload and print its record (for profiling)")
+                    help="run one workload and print its record (for profiling; no oracle)")
     ap.add_argument("--prefill-reps", type=int, default=2)
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -546,58 +747,29 @@ def main(argv=None):
         c = synth.CONFIGS[args.only]
         _log(f"[bench] only {c.name}")
         if args.only.startswith("C4"):
-            rec = prefill_record(c, args.prefill_reps)
+            rec, _ = prefill_record(c, args.prefill_reps)
         else:
-            rec, _ = decode_record(c, args.steps, args.warmup,
-                                   PARTITION_BLOCKS[args.only])
+            rec, _ = decode_record(c, args.steps, args.warmup, PARTITION_BLOCKS[args.only])
         print(json.dumps(rec), flush=True)
         return 0
-    cfg = synth.CONFIGS["C2"]
-    _log(f"[bench] headline {cfg.name}: warmup {args.warmup}, steps {args.steps}")
-    head, st = decode_record(cfg, args.steps, args.warmup, 0)
-    del st
-    torch.cuda.empty_cache()
-    _log(f"[bench] {head['tok_per_s']:.0f} tok/s, decode {head['roofline']['achieved']:.0f} GB/s")
 
+    # headline: the 128K decode, with the 128K chunked prefill beside it
+    head = decode_with_baseline("C3", args)
+    pre128 = prefill_with_baseline("C4_128K", args)
     secondary = []
     if not args.no_secondary:
-        for name in ("C3", "C5"):
-            pb = PARTITION_BLOCKS[name]
-            c = synth.CONFIGS[name]
-            _log(f"[bench] secondary {c.name}")
-            rec, st = decode_record(c, args.steps, args.warmup, pb)
-            del st
-            torch.cuda.empty_cache()
-            rec["partition_blocks"] = pb
-            secondary.append(rec)
-            _log(f"[bench]   {rec['tok_per_s']:.0f} tok/s, {rec['roofline']['achieved']:.0f} GB/s")
-
-        for name in ("C4", "C4_128K", "C4_FP8"):
-            c = synth.CONFIGS[name]
-            _log(f"[bench] secondary {c.name}")
-            rec = prefill_record(c, args.prefill_reps)
-            if name == "C4" and not args.no_cpu_baseline:
-                rec["cpu_baseline"] = cpu_baseline_prefill(c, args.cpu_seconds / 2)
-                rec["cpu_baseline"]["gpu_speedup"] = rec["tflops"] / rec["cpu_baseline"]["value"]
-            secondary.append(rec)
-            _log(f"[bench]   {rec['tflops']:.0f} TFLOP/s, {rec['ms_per_prompt']:.2f} ms/prompt; "
-                 f"kv_append {rec['kv_append']['gbs']:.0f} GB/s")
-
-    if not args.no_secondary:
+        for name in ("C2", "C5"):
+            secondary.append(decode_with_baseline(name, args))
+        for name in ("C4", "C4_FP8"):
+            secondary.append(prefill_with_baseline(name, args))
         bc = block_copy_record()
         secondary.append(bc)
         _log(f"[bench] block copies: offload {bc['offload_gbs']:.1f} GB/s, page-in "
              f"{bc['page_in_gbs']:.1f} GB/s, in HBM {bc['hbm_copy_gbs_read_plus_write']:.0f} GB/s")
-
     copy = hbm_copy_record()
     _log(f"[bench] plain device copy: {copy['gbs']:.0f} GB/s")
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        _log("[bench] cpu baseline (fp64 oracle)")
-        cpu = cpu_baseline_decode(cfg, args.cpu_seconds)
-        cpu["gpu_speedup"] = head["tok_per_s"] / cpu["value"]
-
+    cfg = synth.CONFIGS["C3"]
     line = {
         "metric": METRIC,
         "value": head["tok_per_s"],
@@ -614,13 +786,16 @@ def main(argv=None):
         "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_lens[0],
                    "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
                    "block_size": 16, "kv_dtype": cfg.kv_dtype, "pool_blocks": cfg.pool_blocks,
-                   "step": "append 1 token/seq folded into split-KV decode (pkv_paged_attn_decode_step) + LSE merge"},
+                   "partition_blocks": PARTITION_BLOCKS["C3"],
+                   "step": "append 1 token/seq folded into split-KV decode "
+                           "(pkv_paged_attn_decode_step) + LSE merge"},
         "ms_per_step_no_events": head["ms_per_step_no_events"],
         "merge_ms": head["merge_ms"],
         "decode_hbm_gbs": head["roofline"]["achieved"],
         "hbm_copy_gbs": copy["gbs"],
         "roofline": head["roofline"],
-        "cpu_baseline": cpu,
+        "cpu_baseline": head.get("cpu_baseline"),
+        "prefill_128k": pre128,
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)

@@ -156,39 +156,23 @@ def test_fp8_prefill_row_equals_fp8_decode(lib):
 
 
 def test_fp8_chunked_prefill_sampled(lib):
-    """The 32768-token prompt over an E4M3 pool, as bench.py runs it: per
-    4096-token chunk, the chunk's scales and append, then attention over
-    8192-token shards merged by LSE; sampled rows (each shard's first and
-    last included) against the oracle."""
+    """The 32768-token prompt over an E4M3 pool through bench.py's own chunked
+    pass (per 4096-token chunk, the chunk's scales and append, then attention
+    over 8192-token shards merged by LSE), pool poisoned with NaN codes;
+    sampled rows (each shard's first and last included) against the oracle."""
+    import bench
+
     cfg = synth.CONFIGS["C4_FP8"]
     rows = np.array([0, 1, 63, 64, 4095, 4096, 8191, 8192, 16000, 24575, 30001, 32767])
-    inp = synth.prefill_inputs(cfg, device=DEV)
-    tables, _ = lib.build_tables([cfg.prompt_len], cfg.pool_blocks, inp["free_order"])
-    td = tables.to(DEV)
-    cache = lib.PagedCache.empty(cfg.pool_blocks, cfg.hkv, 128, "e4m3", fill=0x7F)
-    outs = torch.empty_like(inp["q"])
-    C, S = cfg.chunk, cfg.shard_len
-    for c in range(cfg.num_chunks):
-        a, b = c * C, (c + 1) * C
-        lib.fp8_group_scales(cache, inp["k"][a:b], inp["v"][a:b], a, td[0])
-        lib.kv_append(cache, inp["k"][a:b], inp["v"][a:b],
-                      torch.zeros(C, dtype=torch.int32, device=DEV),
-                      torch.arange(a, b, dtype=torch.int32, device=DEV), td)
-        q = inp["q"][a:b]
-        shards = [(j * S, min((j + 1) * S, b)) for j in range(b // S + (1 if b % S else 0))]
-        if len(shards) == 1:                     # as bench.py: final form, nothing to merge
-            lib.paged_attn_prefill(cache, q, a, td[0], 0, b, True, out=outs[a:b])
-            continue
-        parts = [lib.paged_attn_prefill(cache, q, a, td[0], s0, s1, True, partial=True)
-                 for s0, s1 in shards]
-        lib.attn_lse_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]),
-                           torch.stack([p[2] for p in parts]), out=outs[a:b], with_state=False)
+    st = bench.prefill_setup(cfg, poison=True)
+    bench.prefill_pass(cfg, st)
     torch.cuda.synchronize()
-    tab = tables.numpy()
+    tab = st["tables"].numpy()
+    inp = st["inp"]
     oc = _oracle8(cfg, {"k": inp["k"].cpu(), "v": inp["v"].cpu()}, tab)
     sel = torch.from_numpy(rows).to(DEV)
     qs = bits(inp["q"][sel])
-    got = outs[sel].float().cpu().numpy()
+    got = st["out"][sel].float().cpu().numpy()
     for i, r in enumerate(rows):
         ref = O.prefill(oc, qs[i:i + 1], "bf16", int(r), tab[0], 0, int(r) + 1, True)
         compare_rows(got[i:i + 1], ref["o"], "e4m3", f"C4 FP8 row {r}")
