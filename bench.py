@@ -450,6 +450,102 @@ def block_copy_record(reps=5, blocks=8192, cow_blocks=32):
     return rec
 
 
+def page_in_overlap_record(steps=20, warmup=3, blocks=2048, reps=3):
+    """The prefetch of KV offload beside decode: C2 decode steps (the folded
+    step + merge, as timed for the C2 record) on the current stream while
+    pkv_copy_blocks pages `blocks` blocks (C2's format, 64 KiB each) in from a
+    pinned host pool on a second stream.  Reported: the decode steps alone,
+    the page-in alone, both together (from one start event to the later of
+    the two ends), the overlap fraction (t_decode + t_page_in - t_both) /
+    min(t_decode, t_page_in), and the decode kernel's GB/s while the page-in
+    runs.  Medians over `reps` repetitions of each."""
+    import statistics
+    import torch
+    import synth
+    from paged_kv_cache_210_amd import accounting as A
+    from paged_kv_cache_210_amd import lib
+
+    cfg = synth.CONFIGS["C2"]
+    st = _decode_setup(cfg, 0)
+    s_in = st["step_in"]
+    po, pm, pl = st["part"]
+    it = [0]
+
+    def step(ev=None):
+        cache = st["caches"][it[0] % 2]
+        it[0] += 1
+        if ev is not None:
+            ev[0].record()
+        lib.paged_attn_decode_step(cache, s_in["k"], s_in["v"], st["q"], st["td"], st["lens"],
+                                   partial=True, part=st["part"])
+        if ev is not None:
+            ev[1].record()
+        lib.attn_lse_merge(po, pm, pl, out=st["out"], with_state=False, out_lse=st["lse"])
+
+    hkv, d = cfg.hkv, cfg.head_dim
+    host = lib.PagedCache.empty(blocks, hkv, d, "bf16", pinned=True)
+    host.k.copy_(torch.randn(host.k.shape).to(torch.bfloat16))
+    host.v.copy_(torch.randn(host.v.shape).to(torch.bfloat16))
+    dst = lib.PagedCache.empty(blocks, hkv, d, "bf16")
+    perm = torch.randperm(blocks, generator=torch.Generator().manual_seed(8)).to(torch.int32)
+    src_ids = perm.cuda()
+    dst_ids = torch.arange(blocks, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    E = lambda: torch.cuda.Event(enable_timing=True)    # noqa: E731
+
+    def run(decode, page_in):
+        torch.cuda.synchronize()
+        t0, end_m, end_s = E(), E(), E()
+        evs = [[E(), E()] for _ in range(steps)] if decode else []
+        t0.record(main)
+        side.wait_event(t0)
+        if page_in:
+            lib.copy_blocks(host, dst, src_ids, dst_ids, stream=side)
+        end_s.record(side)
+        if decode:
+            for i in range(steps):
+                step(evs[i])
+        end_m.record(main)
+        torch.cuda.synchronize()
+        both = max(t0.elapsed_time(end_m), t0.elapsed_time(end_s))
+        dec = sum(e[0].elapsed_time(e[1]) for e in evs)
+        return both, dec
+
+    for _ in range(warmup):
+        step()
+    run(True, True)
+    t_dec, t_pg, t_both, k_alone, k_both = [], [], [], [], []
+    for _ in range(reps):
+        b, k = run(True, False)
+        t_dec.append(b)
+        k_alone.append(k)
+        t_pg.append(run(False, True)[0])
+        b, k = run(True, True)
+        t_both.append(b)
+        k_both.append(k)
+    med = statistics.median
+    td, tp, tb = med(t_dec), med(t_pg), med(t_both)
+    kbytes = A.decode_kernel_bytes(cfg.seq_lens, cfg.hq, cfg.hkv, cfg.head_dim, cfg.q_dtype,
+                                   cfg.kv_dtype)
+    kbytes += A.append_bytes(cfg.batch, cfg.hkv, cfg.head_dim, cfg.kv_dtype) - 8 * cfg.batch
+    moved = blocks * A.block_bytes(hkv, d, "bf16")
+    rec = {
+        "workload": f"{cfg.name}: {steps} decode steps on one stream while {blocks} blocks "
+                    f"({moved / 2**20:.0f} MiB) page in from pinned host memory on another",
+        "decode_alone_ms": td, "page_in_alone_ms": tp, "both_ms": tb,
+        "overlap_frac": (td + tp - tb) / min(td, tp),
+        "page_in_gbs_alone": moved / (tp * 1e-3) / 1e9,
+        "decode_gbs_alone": kbytes * steps / (med(k_alone) * 1e-3) / 1e9,
+        "decode_gbs_during_page_in": kbytes * steps / (med(k_both) * 1e-3) / 1e9,
+        "decode_tok_per_s_during_page_in": cfg.batch * steps / (tb * 1e-3),
+        "reps": reps,
+    }
+    del st, host, dst
+    torch.cuda.empty_cache()
+    return rec
+
+
 def hbm_copy_record(reps=20, nbytes=1 << 30):
     """A plain device-to-device copy of a known size: the attainable-bandwidth
     context for the decode roofline, and the reference kernel for scaling the
@@ -722,7 +818,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU budget unit of the oracle baselines (each takes a share)")
     ap.add_argument("--only", choices=["C2", "C3", "C5", "C4", "C4_128K", "C4_FP8", "hbm_copy",
-                                       "block_copy"],
+                                       "block_copy", "page_in_overlap"],
                     help="run one workload and print its record (for profiling; no oracle)")
     ap.add_argument("--prefill-reps", type=int, default=2)
     args = ap.parse_args(argv)
@@ -742,6 +838,9 @@ def main(argv=None):
         return 0
     if args.only == "block_copy":
         print(json.dumps(block_copy_record()), flush=True)
+        return 0
+    if args.only == "page_in_overlap":
+        print(json.dumps(page_in_overlap_record(args.steps, args.warmup)), flush=True)
         return 0
     if args.only:
         c = synth.CONFIGS[args.only]
@@ -766,6 +865,11 @@ def main(argv=None):
         secondary.append(bc)
         _log(f"[bench] block copies: offload {bc['offload_gbs']:.1f} GB/s, page-in "
              f"{bc['page_in_gbs']:.1f} GB/s, in HBM {bc['hbm_copy_gbs_read_plus_write']:.0f} GB/s")
+        ov = page_in_overlap_record(args.steps, args.warmup)
+        secondary.append(ov)
+        _log(f"[bench] page-in beside decode: overlap {ov['overlap_frac']:.2f}, decode "
+             f"{ov['decode_gbs_during_page_in']:.0f} GB/s during the page-in "
+             f"({ov['decode_gbs_alone']:.0f} alone), page-in {ov['page_in_gbs_alone']:.1f} GB/s")
     copy = hbm_copy_record()
     _log(f"[bench] plain device copy: {copy['gbs']:.0f} GB/s")
 

@@ -374,12 +374,14 @@ extern "C" int32_t pkv_attn_lse_merge(int32_t S, int64_t rows, int32_t head_dim,
 
 // Memory a kernel may address: device memory, or host memory pinned and
 // mapped for the device.  Pageable host memory is refused before any launch.
-bool device_addressable(const void* p) {
+// *host tells whether the memory is on the host side of PCIe.
+bool device_addressable(const void* p, bool* host) {
   hipPointerAttribute_t at{};
   if (hipPointerGetAttributes(&at, p) != hipSuccess) {
     (void)hipGetLastError();          // do not leave the failed query as a sticky error
     return false;
   }
+  *host = at.type == hipMemoryTypeHost;
   return at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeHost ||
          at.type == hipMemoryTypeManaged || at.type == hipMemoryTypeUnified;
 }
@@ -399,8 +401,12 @@ extern "C" int32_t pkv_copy_blocks(const pkv_cache_desc* src, const pkv_cache_de
   const bool f8 = src->kv_dtype == PKV_FP8_E4M3;
   const void* need[] = {src->k_cache, src->v_cache, dst->k_cache, dst->v_cache, src_ids, dst_ids,
                         src->k_scale, src->v_scale, dst->k_scale, dst->v_scale};
-  for (int i = 0; i < (f8 ? 10 : 6); ++i)
-    if (!device_addressable(need[i])) return PKV_ERR_INVALID_ARG;
+  bool host_pool = false;
+  for (int i = 0; i < (f8 ? 10 : 6); ++i) {
+    bool host = false;
+    if (!device_addressable(need[i], &host)) return PKV_ERR_INVALID_ARG;
+    if (i < 4) host_pool |= host;
+  }
   const int es = elem_size(src->kv_dtype);
   pkv::CopyArgs a{};
   a.src_k = static_cast<const uint8_t*>(src->k_cache);
@@ -419,7 +425,7 @@ extern "C" int32_t pkv_copy_blocks(const pkv_cache_desc* src, const pkv_cache_de
   a.dst_blocks = dst->num_blocks;
   a.src_ids = src_ids;
   a.dst_ids = dst_ids;
-  return from_hip(pkv::launch_copy_blocks(a, n, stream_of(stream)));
+  return from_hip(pkv::launch_copy_blocks(a, n, stream_of(stream), host_pool));
 }
 
 extern "C" int32_t pkv_validate_tables(const int32_t* block_tables, const int32_t* seq_lens,

@@ -162,7 +162,8 @@ struct CopyArgs {
   const int32_t* src_ids;
   const int32_t* dst_ids;
 };
-hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t s);
+// host_pool: one of the pools is in host memory (the copy crosses PCIe).
+hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t s, bool host_pool);
 
 // Generic strided merge of S partial states per row.
 struct MergeArgs {
