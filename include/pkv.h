@@ -282,6 +282,20 @@ int32_t pkv_fp8_group_scales(const pkv_cache_desc* cache, const void* k_src, con
                              int32_t src_dtype, int32_t num_tokens, int32_t pos0,
                              const int32_t* table_row, int32_t max_blocks, void* stream);
 
+/* ---- FP8 group scales and append in one pass [P2 3.2, P1 2.2] -------------
+ * pkv_fp8_group_scales over one sequence's tokens [pos0, pos0 + num_tokens)
+ * followed by pkv_kv_append of the same tokens (token i at position pos0 + i
+ * of the sequence whose table is table_row), reading each source row once:
+ * the pool and the scales end bit for bit as after the two calls.  Arguments
+ * and requirements as pkv_fp8_group_scales (E4M3 cache, pos0 % 64 == 0, bf16
+ * or f32 sources [num_tokens][num_kv_heads][head_dim], 16-byte aligned);
+ * tokens whose block id is outside the pool are skipped, as by
+ * pkv_kv_append.  The append of a prompt chunk into an E4M3 pool. */
+int32_t pkv_kv_append_fp8_groups(const pkv_cache_desc* cache, const void* k_new,
+                                 const void* v_new, int32_t src_dtype, int32_t num_tokens,
+                                 int32_t pos0, const int32_t* table_row, int32_t max_blocks,
+                                 void* stream);
+
 /* ---- split-KV decode [P2 5.1, P3 1.1, P1 3.1, P4 incremental softmax] ----
  * One query per sequence b (the newest token, already appended) attends to
  * every key t < seq_lens[b] of that sequence:

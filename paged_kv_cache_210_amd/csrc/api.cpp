@@ -113,6 +113,26 @@ extern "C" int32_t pkv_fp8_group_scales(const pkv_cache_desc* cache, const void*
                                                max_blocks, stream_of(stream)));
 }
 
+extern "C" int32_t pkv_kv_append_fp8_groups(const pkv_cache_desc* cache, const void* k_new,
+                                            const void* v_new, int32_t src_dtype,
+                                            int32_t num_tokens, int32_t pos0,
+                                            const int32_t* table_row, int32_t max_blocks,
+                                            void* stream) {
+  int32_t st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (cache->kv_dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (src_dtype != PKV_F32 && src_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || pos0 < 0 || (pos0 % PKV_SCALE_GROUP) || max_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !table_row || !aligned16(k_new) || !aligned16(v_new))
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)pos0 + num_tokens > (int64_t)max_blocks * PKV_BLOCK_SIZE) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_fp8_group_append(view(cache), cache->k_scale, cache->v_scale, k_new,
+                                               v_new, src_dtype, num_tokens, pos0, table_row,
+                                               max_blocks, stream_of(stream)));
+}
+
 extern "C" int32_t pkv_decode_workspace_bytes(const pkv_cache_desc* cache, int32_t q_dtype,
                                               int32_t B, int32_t num_q_heads,
                                               int32_t max_blocks_per_seq,

@@ -57,6 +57,20 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | code;
 }
 
+// e4m3_encode of two values at once, a in bits 0-7 and b in bits 8-15, on the
+// hardware pair convert (OCP E4M3, round to nearest even): the inputs are
+// clamped to +-448 first, so that larger magnitudes and infinities saturate,
+// and NaN becomes 0x7F afterwards.  The result equals e4m3_encode's for every
+// fp32 input (compared over all 2^32 bit patterns on gfx950).
+__device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
+  const float ca = fminf(fmaxf(a, -448.0f), 448.0f);
+  const float cb = fminf(fmaxf(b, -448.0f), 448.0f);
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xffffu;
+  if (a != a) r = (r & 0xff00u) | 0x7fu;
+  if (b != b) r = (r & 0x00ffu) | 0x7f00u;
+  return r;
+}
+
 // Fragment-order pages (bf16 and E4M3 pools): byte offset of the element of
 // token t, dimension d inside one (block, kv head) page of ES-byte elements.
 // Lane l = 16*g + i of a decode wave finds all of its matrix-instruction
@@ -108,6 +122,12 @@ hipError_t launch_kv_append(const CacheView& c, void* k_pool, void* v_pool, cons
                             const void* v_new, int src_dtype, int num_tokens,
                             const int32_t* seq_idx, const int32_t* pos, const int32_t* tables,
                             int num_seqs, int maxb, hipStream_t s);
+// launch_fp8_group_scales + launch_kv_append of one sequence's tokens
+// [pos0, pos0 + num_tokens) in one pass (each source row read once).
+hipError_t launch_fp8_group_append(const CacheView& c, float* k_scale, float* v_scale,
+                                   const void* k_src, const void* v_src, int src_dtype,
+                                   int num_tokens, int pos0, const int32_t* table_row, int maxb,
+                                   hipStream_t s);
 hipError_t launch_fp8_group_scales(const CacheView& c, float* k_scale, float* v_scale,
                                    const void* k_src, const void* v_src, int src_dtype,
                                    int num_tokens, int pos0, const int32_t* table_row,

@@ -210,11 +210,12 @@ __device__ __forceinline__ void put_piece(uint8_t* vs, u32x4 vv, int i, int pg, 
 // (their K, whatever it holds, only ever meets the mask).
 template <int D>
 __device__ __forceinline__ void store_tile(uint8_t* buf, uint8_t* meta, const TileRegs<D>& r,
-                                           const PrefillParams& p, int tile, int tid) {
+                                           const PrefillParams& p, int tile, int tid,
+                                           bool flags) {
   uint8_t* vs = buf + Geo<D>::KTILE;
   const int pg = tid >> 7, t128 = tid & 127;
   const int tok_base = tile * BN + pg * kBlock;   // first token of this page
-  if (t128 == 0) meta[16 + pg] = page_usable(p, tile * 4 + pg, r.valid) ? 1 : 0;
+  if (flags && t128 == 0) meta[16 + pg] = page_usable(p, tile * 4 + pg, r.valid) ? 1 : 0;
   const bool boundary = tile * BN < p.kv_begin || tile * BN + BN > p.kv_end;
   if (r.valid && !boundary) {                      // uniform over the wave
 #pragma unroll
@@ -317,7 +318,8 @@ __device__ __forceinline__ void load_tile(TileRegs8<D>& r, uint8_t*, const Prefi
 // scales there do not leak).
 template <int D>
 __device__ __forceinline__ void store_tile(uint8_t* buf, uint8_t* meta, const TileRegs8<D>& r,
-                                           const PrefillParams& p, int tile, int tid) {
+                                           const PrefillParams& p, int tile, int tid,
+                                           bool flags) {
   float* ks_slot = reinterpret_cast<float*>(meta);
   constexpr int W8 = Geo<D>::W8;
   uint8_t* vs = buf + Geo<D>::KTILE;
@@ -333,7 +335,7 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, uint8_t* meta, const Ti
   }
   if (t128 == 0) {
     ks_slot[pg] = r.valid ? r.ks : 1.0f;
-    meta[16 + pg] = page_usable(p, tile * 4 + pg, r.valid) ? 1 : 0;
+    if (flags) meta[16 + pg] = page_usable(p, tile * 4 + pg, r.valid) ? 1 : 0;
   }
   const int tok_base = tile * BN + pg * kBlock;   // first token of this page
   const bool plain = r.valid && !(tile * BN < p.kv_begin || tile * BN + BN > p.kv_end);
@@ -358,13 +360,15 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, uint8_t* meta, const Ti
   }
 }
 
-// Stores a staged tile into ring slot `slot`, and its page flags (and, for
-// E4M3 pools, its K scales) into the slot's entry after the ring.
+// Stores a staged tile into ring slot `slot`, and (when `flags`: some page
+// of the workgroup's range is unusable) its page flags, and for E4M3 pools
+// its K scales, into the slot's entry after the ring.
 template <int D, typename Regs>
 __device__ __forceinline__ void stage_store(uint8_t* smem, int slot, const Regs& r,
-                                            const PrefillParams& p, int tile, int tid) {
+                                            const PrefillParams& p, int tile, int tid,
+                                            bool flags) {
   store_tile(smem + slot * Geo<D>::BUF, smem + Geo<D>::LDS + Geo<D>::META * slot, r, p, tile,
-             tid);
+             tid, flags);
 }
 
 // The four page flags of the tile in ring slot `slot` (byte i = page i),
@@ -631,6 +635,15 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
   const int t_hi = key_end > p.kv_begin ? (key_end - 1) / BN : t_lo - 1;
   const int w_minpos = p.q_pos0 + wrow0;
 
+  // Does any page this workgroup reads have an id outside the pool inside the
+  // key range?  Checked once over the table; only then do the steps read the
+  // per-slot page flags (otherwise no step waits on that LDS read).
+  bool any_bad = false;
+  if (t_lo <= t_hi)
+    for (int lb = t_lo * 4 + tid; lb < min((t_hi + 1) * 4, p.maxb); lb += NTHREADS)
+      any_bad |= !page_usable(p, lb, (unsigned)p.table[lb] < (unsigned)p.num_blocks);
+  any_bad = __syncthreads_or(any_bad);
+
   RowState<D> st;
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt)
@@ -644,10 +657,10 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
   if (t_lo <= t_hi) {
     Regs regs;
     load_tile(regs, smem, p, t_lo, tile_entry(p, t_lo, tid), tid, kvh);
-    stage_store<D>(smem, 0, regs, p, t_lo, tid);
+    stage_store<D>(smem, 0, regs, p, t_lo, tid, any_bad);
     if (t_lo + 1 <= t_hi) {
       load_tile(regs, smem + G::BUF, p, t_lo + 1, tile_entry(p, t_lo + 1, tid), tid, kvh);
-      stage_store<D>(smem, 1, regs, p, t_lo + 1, tid);
+      stage_store<D>(smem, 1, regs, p, t_lo + 1, tid, any_bad);
     }
     int entry_next = tile_entry(p, t_lo + 2, tid);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct-to-LDS K loads are in
@@ -656,7 +669,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
     f32x16 sa[2], sb[2];
     qk_tile<D, F8>(sa, smem, qf, qr, hi);
     if (tile_needs_mask(p, t_lo * BN, w_minpos)) mask_tile<NEG_SCALE>(sa, p, t_lo * BN, my_pos, hi);
-    {
+    if (any_bad) {
       const uint32_t fl = page_flags<D>(smem, 0);
       if (fl != kAllPagesUsable) mask_pages<NEG_SCALE>(sa, fl);
     }
@@ -671,18 +684,20 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillParams p) {
       const int s1 = slot == 2 ? 0 : slot + 1;
       const int s2 = s1 == 2 ? 0 : s1 + 1;
       const bool prefetch = j + 2 <= t_hi;
-      const uint32_t fl_next = page_flags<D>(smem, s1);   // tile j+1, published last step
       Regs nregs;
       if (prefetch) load_tile(nregs, smem + s2 * G::BUF, p, j + 2, entry_next, tid, kvh);
       entry_next = tile_entry(p, j + 3, tid);
       attend_step<D, NEG_SCALE, F8>(st, s_cur, s_next, smem + slot * G::BUF, smem + s1 * G::BUF,
                                     qf, c, reinterpret_cast<const float*>(smem + G::LDS + G::META * slot),
                                     qr, hi);
-      if (prefetch) stage_store<D>(smem, s2, nregs, p, j + 2, tid);
+      if (prefetch) stage_store<D>(smem, s2, nregs, p, j + 2, tid, any_bad);
       if (j + 1 <= t_hi) {
         if (tile_needs_mask(p, (j + 1) * BN, w_minpos))
           mask_tile<NEG_SCALE>(s_next, p, (j + 1) * BN, my_pos, hi);
-        if (fl_next != kAllPagesUsable) mask_pages<NEG_SCALE>(s_next, fl_next);
+        if (any_bad) {                     // tile j+1's flags, published last step
+          const uint32_t fl = page_flags<D>(smem, s1);
+          if (fl != kAllPagesUsable) mask_pages<NEG_SCALE>(s_next, fl);
+        }
       }
       slot = s1;
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct-to-LDS K loads are in

@@ -87,6 +87,8 @@ _SIGS = {
                                 c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p]),
     "pkv_fp8_group_scales": (c_int32, [POINTER(CacheDesc), c_void_p, c_void_p, c_int32, c_int32,
                                        c_int32, c_void_p, c_int32, c_void_p]),
+    "pkv_kv_append_fp8_groups": (c_int32, [POINTER(CacheDesc), c_void_p, c_void_p, c_int32,
+                                           c_int32, c_int32, c_void_p, c_int32, c_void_p]),
     "pkv_decode_workspace_bytes": (c_int32, [POINTER(CacheDesc), c_int32, c_int32, c_int32,
                                              c_int32, c_int32, POINTER(c_size_t)]),
     "pkv_paged_attn_decode": (c_int32, [POINTER(CacheDesc), c_void_p, c_int32, c_int32, c_int32,
@@ -397,6 +399,24 @@ def fp8_group_scales(cache: PagedCache, k_src, v_src, pos0, table_row):
     _check(load().pkv_fp8_group_scales(ctypes.byref(d), _p(k_src), _p(v_src),
                                        -1 if src is None else src, T, int(pos0), _p(table_row),
                                        table_row.numel(), _stream(dev)), "fp8_group_scales")
+
+
+def kv_append_fp8_groups(cache: PagedCache, k_new, v_new, pos0, table_row):
+    """pkv_kv_append_fp8_groups: the group scales and the append of one
+    sequence's tokens [pos0, pos0 + T) into an E4M3 pool in one pass."""
+    dev = cache.device
+    T = k_new.shape[0]
+    src = _DTYPE_CODE.get(k_new.dtype)
+    if src is None:
+        raise TypeError("k_new must be float32 or bfloat16")
+    shape = (T, cache.hkv, cache.head_dim)
+    _need(k_new, None, "k_new", dev, shape)
+    _need(v_new, k_new.dtype, "v_new", dev, shape)
+    _need(table_row, torch.int32, "table_row", dev)
+    d = cache.desc()
+    _check(load().pkv_kv_append_fp8_groups(ctypes.byref(d), _p(k_new), _p(v_new), src, T,
+                                           int(pos0), _p(table_row), table_row.numel(),
+                                           _stream(dev)), "kv_append_fp8_groups")
 
 
 def decode_workspace_bytes(cache: PagedCache, q_dtype, B, hq, max_blocks, partition_blocks=0):

@@ -431,3 +431,55 @@ def test_fp8_group_scales_aligned_unaligned_and_f32_sources_agree(lib):
     for gk, gv in got:
         np.testing.assert_array_equal(gk, ref_k)
         np.testing.assert_array_equal(gv, ref_v)
+
+
+@pytest.mark.parametrize("src,d,n,pos0", [("bf16", 128, 4096, 0), ("bf16", 128, 200, 128),
+                                          ("f32", 128, 130, 64), ("bf16", 64, 320, 0),
+                                          ("f32", 64, 64, 192), ("bf16", 128, 17, 0)])
+def test_fused_fp8_group_append_equals_scales_then_append(lib, src, d, n, pos0):
+    """pkv_kv_append_fp8_groups (scales and append in one pass) against
+    pkv_fp8_group_scales + pkv_kv_append, bit for bit over the whole pool and
+    both scale arrays, and against the oracle; the table names one block
+    outside the pool inside the tokens (its tokens are skipped, its group's
+    other blocks still get the scale) and blocks past the tokens (a partial
+    last group's span reaches them)."""
+    hkv = 4
+    L = pos0 + n
+    cfg = synth.decode_config("fused", (L,), 16, hkv, d, kv_dtype="e4m3", seed_index=34,
+                              outlier_prob=0.01)
+    inp = synth.decode_inputs(cfg)
+    nbl = -(-L // 16) + 4                                   # 4 more table entries than needed
+    pool = cfg.pool_blocks + 8
+    order = synth.free_order(pool, 35)
+    table = order[:nbl].clone()
+    if nbl > 6:
+        table[5] = pool + 3                                 # a block outside the pool
+    td = table.to(DEV)
+    k = inp["k"][pos0:L].to(DEV)
+    v = inp["v"][pos0:L].to(DEV)
+    if src == "f32":
+        k, v = k.float(), v.float()
+    fused = lib.PagedCache.empty(pool, hkv, d, "e4m3", fill=0x7F)
+    twice = lib.PagedCache.empty(pool, hkv, d, "e4m3", fill=0x7F)
+    lib.kv_append_fp8_groups(fused, k, v, pos0, td)
+    lib.fp8_group_scales(twice, k, v, pos0, td)
+    lib.kv_append(twice, k, v, torch.zeros(n, dtype=torch.int32, device=DEV),
+                  torch.arange(pos0, L, dtype=torch.int32, device=DEV), td[None])
+    torch.cuda.synchronize()
+    for a, b in ((fused.k, twice.k), (fused.v, twice.v), (fused.k_scale, twice.k_scale),
+                 (fused.v_scale, twice.v_scale)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    oc = O.new_cache(pool, hkv, d, "e4m3")
+    oc.k[...] = 0x7F
+    oc.v[...] = 0x7F
+    kf, vf = k.float().cpu().numpy(), v.float().cpu().numpy()
+    tn = table.numpy()
+    O.fp8_group_scales(kf, pos0, tn, oc.k_scale)
+    O.fp8_group_scales(vf, pos0, tn, oc.v_scale)
+    ok = [i for i in range(n) if 0 <= tn[(pos0 + i) // 16] < pool]
+    O.append(oc, kf[ok], vf[ok], np.zeros(len(ok), np.int32), np.array([pos0 + i for i in ok]),
+             tn[None])
+    gk, gv = frag_pages_logical(fused.k.cpu().numpy(), fused.v.cpu().numpy(), 1)
+    assert np.array_equal(gk, oc.k) and np.array_equal(gv, oc.v)
+    assert np.array_equal(fused.k_scale.cpu().numpy(), oc.k_scale)
+    assert np.array_equal(fused.v_scale.cpu().numpy(), oc.v_scale)
