@@ -114,6 +114,91 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   }
 }
 
+// A moderate number of parts (a decode split into 17 .. 16 * (512 / (D / 4))
+// partitions, e.g. 32 at 128K or 256 at 1M tokens): one workgroup of 512
+// threads per row, groups of D/4 threads each owning 4 dimensions; thread
+// (group g, lane) takes parts g, g + NG, ... (PPT of them) and issues every
+// load of m, l and O~ at once, so the row costs one memory round trip, then
+// one block-wide max and one block-wide sum.  Parts past S repeat the last
+// part's address and are selected away, as are parts with no visible key.
+template <int PPT>
+__global__ __launch_bounds__(kMergeThreads) void merge_parts_kernel(MergeArgs a) {
+  constexpr int NW = kMergeThreads / 64;
+  __shared__ float redm[NW];
+  __shared__ float redl[NW];
+  __shared__ f32x4 osum[kMergeThreads];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lanes = a.D >> 2;                        // threads per group
+  const int ng = kMergeThreads / lanes;              // groups
+  const int gi = tid / lanes, li = tid - gi * lanes;
+  const float* mrow = a.m + row * a.ml_row;
+  const float* lrow = a.l + row * a.ml_row;
+  const float* orow = a.o + row * a.o_row + 4 * li;
+  const float f = kLog2e;               // m in natural units
+  float ms[PPT], ls[PPT];
+  f32x4 ov[PPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int sc = min(gi + ng * k, a.S - 1);
+    ms[k] = mrow[sc * a.ml_part];
+    ls[k] = lrow[sc * a.ml_part];
+    ov[k] = *reinterpret_cast<const f32x4*>(orow + (int64_t)sc * a.o_part);
+  }
+  bool live[PPT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    live[k] = gi + ng * k < a.S && ls[k] > 0.f && ms[k] > -INFINITY;
+    if (live[k]) mx = fmaxf(mx, ms[k]);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) redm[w] = mx;
+  __syncthreads();
+  float M = redm[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, redm[i]);
+  const bool any = M > -INFINITY;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    if (any && live[k]) {
+      const float ws = __builtin_amdgcn_exp2f((ms[k] - M) * f);
+      if (li == 0) L += ws * ls[k];                  // each part's l once
+      if (ws != 0.f) acc += ws * ov[k];
+    }
+  }
+  L = wave_sum(L);
+  if (lane == 0) redl[w] = L;
+  osum[tid] = acc;
+  __syncthreads();
+  float Lt = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) Lt += redl[i];
+  const bool empty = !any || !(Lt > 0.f);
+  if (tid < lanes) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < ng; ++g) o += osum[g * lanes + tid];
+    o = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : o / Lt;
+    if (a.out_dtype == PKV_BF16) {
+      u32x2 pk;
+      pk.x = (uint32_t)f32_to_bf16_bits(o.x) | ((uint32_t)f32_to_bf16_bits(o.y) << 16);
+      pk.y = (uint32_t)f32_to_bf16_bits(o.z) | ((uint32_t)f32_to_bf16_bits(o.w) << 16);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + row * a.D + 4 * tid) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + row * a.D + 4 * tid) = o;
+    }
+  }
+  if (tid == 0) {
+    const float Mn = empty ? -INFINITY : M;
+    if (a.out_m) a.out_m[row] = Mn;
+    if (a.out_l) a.out_l[row] = empty ? 0.f : Lt;
+    if (a.out_lse) a.out_lse[row] = empty ? -INFINITY : Mn + logf(Lt);
+  }
+}
+constexpr int kMaxPartsPerThread = 16;
+
 // Few parts (prefill shards, short decode splits).  Rows are spread over the
 // lanes of a wave, D/4 lanes per row, each lane owning 4 consecutive
 // dimensions (16-byte loads); every part's m and l are read per lane (lanes
@@ -202,6 +287,15 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
 #undef PKV_MERGE_ROWS
       default: return hipErrorInvalidValue;
     }
+  } else if (vec4 && kMergeThreads % (a.D / 4) == 0 &&
+             a.S <= kMaxPartsPerThread * (kMergeThreads / (a.D / 4))) {
+    const int ng = kMergeThreads / (a.D / 4);
+    const int ppt = (a.S + ng - 1) / ng;
+    const dim3 grid((unsigned)a.rows), block(kMergeThreads);
+    if (ppt <= 2) hipLaunchKernelGGL(merge_parts_kernel<2>, grid, block, 0, s, a);
+    else if (ppt <= 4) hipLaunchKernelGGL(merge_parts_kernel<4>, grid, block, 0, s, a);
+    else if (ppt <= 8) hipLaunchKernelGGL(merge_parts_kernel<8>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(merge_parts_kernel<16>, grid, block, 0, s, a);
   } else if (vec4) {
     hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)a.rows), dim3(kMergeThreads), 0, s, a);
   } else {

@@ -287,11 +287,14 @@ def test_decode_c5_full_size_sampled(lib, pb):
 
 # ------------------------------------------------------------------ merge
 @pytest.mark.parametrize("S,D,rows", [(1, 128, 300), (2, 128, 300), (5, 128, 300), (33, 128, 300),
-                                      (3, 64, 301), (3, 96, 300), (40, 64, 300), (2100, 64, 70)])
+                                      (3, 64, 301), (3, 96, 300), (40, 64, 300), (2100, 64, 70),
+                                      (17, 128, 300), (32, 128, 300), (100, 64, 300),
+                                      (256, 128, 64), (257, 128, 40), (512, 64, 50)])
 def test_lse_merge_matches_oracle(lib, S, D, rows):
-    """Few-part path (several rows per wave), many-part path, a head size that
-    takes the many-part path with few parts (96), and more parts than one LDS
-    chunk of weights (2100)."""
+    """Few-part path (several rows per wave, up to 16 parts); the one-round-trip
+    path for up to 16 parts per thread (17, 32, 33, 40, 100, 256 and, at d 64,
+    512 parts); the chunked many-part path past that (257 at d 128, 2100), and
+    for a head size whose groups do not tile a workgroup (96)."""
     g = torch.Generator().manual_seed(S * 1000 + D)
     o = torch.randn(S, rows, D, generator=g) * 3
     m = torch.randn(S, rows, generator=g) * 4
