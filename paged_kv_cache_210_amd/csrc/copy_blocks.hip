@@ -56,8 +56,10 @@ hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t s, bool host
     // PCIe, not the CUs, bounds a copy to or from host memory: 16 workgroups
     // keep the link busy (56 GB/s measured, as with one workgroup per block)
     // and disturb an attention running beside the copy far less than many
-    // (C2 decode beside a 128 MiB page-in: 73 % of the page-in hidden with
-    // 16, 62 % with 32, 23 % with 64; 8 no longer fill the link).
+    // (8192-token decode of 32 sequences, four-wave workgroups, beside a
+    // 128 MiB page-in: 73 % of the page-in hidden with 16, 62 % with 32, 23 %
+    // with 64; 8 no longer fill the link; beside the two-wave decode, which
+    // leaves no CU idle, 16 hide 54 %).
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(std::min(n, kHostCopyGroups), 1), dim3(CT), 0, s,
                        a, n);
     return hipGetLastError();
