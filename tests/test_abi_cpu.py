@@ -152,6 +152,34 @@ def test_entry_point_argument_checks(lib):
                                 None, None, None) == lib.PKV_ERR_UNSUPPORTED
 
 
+def test_fused_fp8_append_argument_checks(lib):
+    """pkv_kv_append_fp8_groups refuses on the host, before any launch: a
+    cache that is not E4M3, a source that is neither bf16 nor f32, a start not
+    on a 64-token group, tokens past the table, unaligned sources; an empty
+    call returns PKV_OK without touching the device."""
+    L = lib.load()
+    f = L.pkv_kv_append_fp8_groups
+    e4 = _desc(lib, kv_dtype=lib.PKV_FP8_E4M3, block_stride=8 * 16 * 128, k_scale=0x9000,
+               v_scale=0xA000)
+    bf = _desc(lib)
+    assert f(ctypes.byref(bf), 0x3000, 0x4000, lib.PKV_BF16, 64, 0, 0x5000, 4,
+             None) == lib.PKV_ERR_UNSUPPORTED
+    assert f(ctypes.byref(e4), 0x3000, 0x4000, lib.PKV_FP8_E4M3, 64, 0, 0x5000, 4,
+             None) == lib.PKV_ERR_UNSUPPORTED
+    assert f(ctypes.byref(e4), 0x3000, 0x4000, lib.PKV_BF16, 16, 16, 0x5000, 4,
+             None) == lib.PKV_ERR_INVALID_ARG                     # pos0 not a group start
+    assert f(ctypes.byref(e4), 0x3000, 0x4000, lib.PKV_BF16, 65, 0, 0x5000, 4,
+             None) == lib.PKV_ERR_INVALID_ARG                     # 65 tokens, 4 blocks
+    assert f(ctypes.byref(e4), 0x3008, 0x4000, lib.PKV_BF16, 16, 0, 0x5000, 4,
+             None) == lib.PKV_ERR_INVALID_ARG                     # source not 16-byte aligned
+    assert f(ctypes.byref(e4), 0x3000, 0x4000, lib.PKV_BF16, 16, 0, None, 4,
+             None) == lib.PKV_ERR_INVALID_ARG                     # no table
+    assert f(ctypes.byref(e4), 0x3000, 0x4000, lib.PKV_BF16, -1, 0, 0x5000, 4,
+             None) == lib.PKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(e4), 0x3000, 0x4000, lib.PKV_BF16, 0, 0, 0x5000, 4,
+             None) == lib.PKV_OK
+
+
 def test_sharing_allocator_matches_oracle_step_for_step(lib):
     """Fork, copy-on-write growth, prefix publish / match and release through
     the C ABI, against the oracle allocator: same tables, copy pairs,
