@@ -3,8 +3,8 @@ byte against the oracle's encoder ("Unlocking long context ..." section 3.2:
 FP8 E4M3 KV; OCP E4M3FN: round to nearest even, magnitudes beyond 448 saturate,
 NaN -> 0x7F).  The inputs run over all 2^16 values of an fp32's top 16 bits
 (sign, exponent and every mantissa bit at which an E4M3 rounding decision
-falls, the subnormal grid included), each with eight low halves: zero, one,
-the patterns around half of bit 16, all ones and two random ones.  Scales are 1,
+falls, the subnormal grid included), each with eight low halves: 0, 1,
+0x7FFF, 0x8000, 0x8001, 0xFFFF and two random ones.  Scales are 1,
 so the codes are the encoder's own; the whole-page path (page-aligned
 positions) and the per-token path (positions offset by 5) both run."""
 import numpy as np
