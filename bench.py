@@ -7,10 +7,13 @@ split-KV attention of that token against every cached key plus the exact
 log-sum-exp merge (pkv_paged_attn_decode).  Inputs are resident in HBM before
 the timed region starts.
 
-The headline line is the Llama-3-8B-like layer (32 sequences x 8192 tokens,
-32 q / 8 kv heads, d 128, bf16).  The 128K decode, the 1M-token E4M3 decode and
-the chunked causal prefill are reported under "secondary".  The fp64 CPU oracle
-is timed on a bounded sample of the headline workload as "cpu_baseline".
+The headline is the 128K decode (4 sequences x 131072 tokens, 64 q / 8 kv
+heads, d 128, bf16, 256-block partitions); the 131072-token chunked causal
+prefill is carried beside it ("prefill_128k"), and the 8K and 1M-token (E4M3)
+decodes, the 32K prefills (bf16 and E4M3), block copies and the page-in
+overlap are reported under "secondary".  Every decode and prefill record
+carries the fp64 CPU oracle timed on a bounded sample of the same workload
+("cpu_baseline") and the GPU's error against it.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -100,7 +103,8 @@ def bench_decode(cfg, steps, warmup, partition_blocks=0):
     at all (reported beside, not as the value: each event recorded between
     launches costs a few microseconds).  Steps alternate between two pools
     holding the same KV, so no step reads pages still cached from the one
-    before."""
+    before.  Each timed pass is queued behind a GPU spin, so it measures the
+    GPU running the steps back to back, not the host issuing them."""
     import torch
     from paged_kv_cache_210_amd import lib
 
@@ -137,6 +141,11 @@ def bench_decode(cfg, steps, warmup, partition_blocks=0):
         mevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(k)]
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        # the GPU spins (about 8 ms, more for long runs) while the host queues
+        # the k steps, so a pause of the host between two launches (the
+        # Python binding takes longer to issue a C2 step than some of the
+        # steps take) cannot leave the GPU idle inside the timed region
+        torch.cuda._sleep(20_000_000 + 500_000 * k)
         start.record()
         for i in range(k):
             step(evs[i] if dec else None, mevs[i] if merge else None)
