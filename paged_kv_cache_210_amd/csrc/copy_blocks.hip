@@ -21,8 +21,9 @@ constexpr int CT = 256;
 constexpr int kHostCopyGroups = 16;        // workgroups of a copy that crosses PCIe
 
 // Workgroup x takes block pairs x, x + gridDim.x, ... and copies a
-// 1/gridDim.y share of each with 16-byte loads and stores; K and V regions of
-// a block are contiguous runs of `region` bytes in their pools.
+// 1/gridDim.y share of each with 16-byte non-temporal loads and stores (each
+// byte is moved once); K and V regions of a block are contiguous runs of
+// `region` bytes in their pools.
 __global__ __launch_bounds__(CT) void copy_blocks_kernel(CopyArgs a, int n) {
   for (int i = blockIdx.x; i < n; i += gridDim.x) {
     const int sb = a.src_ids[i], db = a.dst_ids[i];
@@ -34,10 +35,10 @@ __global__ __launch_bounds__(CT) void copy_blocks_kernel(CopyArgs a, int n) {
     const int64_t n16 = a.region >> 4;
     for (int64_t o = (int64_t)blockIdx.y * CT + threadIdx.x; o < n16;
          o += (int64_t)CT * gridDim.y) {
-      const u32x4 k = sk[o];
-      const u32x4 v = sv[o];
-      dk[o] = k;
-      dv[o] = v;
+      const u32x4 k = __builtin_nontemporal_load(sk + o);
+      const u32x4 v = __builtin_nontemporal_load(sv + o);
+      __builtin_nontemporal_store(k, dk + o);
+      __builtin_nontemporal_store(v, dv + o);
     }
     if (a.src_ks && blockIdx.y == 0) {
       for (int h = threadIdx.x; h < a.hkv; h += CT) {
